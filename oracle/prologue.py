@@ -1,0 +1,64 @@
+"""Fused RMSNorm + RoPE prologue and latent-cache insert (oracle, test-only).
+
+PR #52046 report, 实现拆解 item 1 and 关键源码片段 (``_fused_norm_rope_kernel``,
+branch ``pid == 1``):
+
+* ``kv_c`` (512 wide) goes through RMSNorm with weight ``w`` and epsilon;
+* ``k_pe`` (64 wide) is rotated in interleaved pairs: for pair i the inputs
+  are elements 2i and 2i+1, ``r1 = x1*cos - x2*sin``, ``r2 = x2*cos + x1*sin``,
+  stored back at 2i and 2i+1;
+* when output buffers are given the results are materialised (bf16);
+* when a slot mapping is given the entry at that slot becomes
+  ``[kv_c (512) | k_pe (64)]``; for an fp8 cache each value is divided by the
+  per-tensor scale and cast to e4m3.
+
+Readings taken where the page is silent:
+* RMSNorm is ``y = x / sqrt(mean(x^2) + eps) * w`` with a plain multiplicative
+  weight, evaluated exactly and rounded once to bf16;
+* the RoPE table row for position p is ``[cos(p*f_0..f_31) | sin(...)]``
+  (the usual cos/sin cache layout), supplied as an fp32 input;
+* "materialised then inserted": the insert quantises the materialised bf16
+  values, so an fp8 entry is ``e4m3(bf16(v) / scale)``;
+* slots < 0 are skipped (padding of a slot mapping).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_to_f64, f64_to_bf16, f64_to_e4m3
+
+D_V = 512
+D_ROPE = 64
+
+
+def rmsnorm_rope(kv_c, k_pe, w, eps, cos_sin, positions):
+    """Returns ``(kv_c_out, k_pe_out)`` as bf16 bits, ``[T][512]`` and ``[T][64]``."""
+    x = bf16_to_f64(kv_c)                                      # [T][512]
+    wv = bf16_to_f64(w)
+    inv_rms = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + np.float64(eps))
+    y = x * inv_rms * wv[None, :]
+    kv_out = f64_to_bf16(y)
+
+    pe = bf16_to_f64(k_pe)                                     # [T][64]
+    cs = np.asarray(cos_sin, dtype=np.float64)[np.asarray(positions, dtype=np.int64)]
+    c, s = cs[:, :D_ROPE // 2], cs[:, D_ROPE // 2:]
+    x1, x2 = pe[:, 0::2], pe[:, 1::2]
+    r = np.empty_like(pe)
+    r[:, 0::2] = x1 * c - x2 * s
+    r[:, 1::2] = x2 * c + x1 * s
+    return kv_out, f64_to_bf16(r)
+
+
+def cache_insert(cache, slot_mapping, kv_c_out, k_pe_out, cache_dtype, scale):
+    """Write the materialised rows into a copy of the cache at their slots."""
+    out = cache.copy()
+    flat = out.reshape(-1, D_V + D_ROPE)
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        entry = np.concatenate([kv_c_out[t], k_pe_out[t]])
+        if cache_dtype == "fp8":
+            flat[slot] = f64_to_e4m3(bf16_to_f64(entry) / np.float64(scale))
+        else:
+            flat[slot] = entry
+    return out
