@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA sparse-attention decode path on one MI355X.
+
+One step = one pass of the whole path over one batch of the decode workload
+(64 rows, 32768-token context, 4 shards, k = 2048, 128 heads, bf16 latent
+cache): per-shard top-K + candidate pack -> merge -> index conversion ->
+sparse MLA decode (all shards) -> LSE combine.  Inputs are resident in HBM
+before timing starts; four independently drawn (logits, q) sets rotate
+through the steps so a step does not find its inputs or its gathered rows
+in the on-chip caches left by the previous step.
+
+Prints ONE JSON line.  `value` = decode tokens/s of the whole path (one query
+token per row); the top-K and decode halves of the metric are reported too,
+with per-kernel times from HIP events recorded on the launch stream over the
+timed steps, the dominant kernel's roofline, and the CPU oracle timed on the
+host for comparison.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer top-K rows/s + sparse-MLA decode tokens/s at 32k ctx, k=2048; % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "tiny", "long", "prefill", "fp8"])
+    p.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def attention_traffic(c, counts_total):
+    """Algorithmic bytes and flops of one sparse_mla_decode launch."""
+    R, H, S, k = c.rows, c.heads, c.S, c.k
+    entry = 576 if c.cache_dtype == "fp8" else 1152
+    bytes_ = (R * H * 576 * 2                 # q, once per row and shard pass
+              + counts_total * entry          # gathered latent rows
+              + counts_total * 4 + S * R * 4  # slot lists + counts
+              + S * R * H * 512 * 2           # bf16 partial outputs
+              + S * R * H * 4)                # partial lse
+    flops = counts_total * H * (576 + 512) * 2
+    return bytes_, flops
+
+
+def topk_traffic(c, n_valid_logits):
+    """Algorithmic bytes of topk_select + merge_candidates for one step."""
+    R, S, k = c.rows, c.S, c.k
+    topk = n_valid_logits * 4 + R * S * k * 8         # logits read, candidates written
+    merge = R * S * k * 8 + R * k * 4                 # candidates read, ids written
+    return topk, merge
+
+
+def cpu_baseline(c, seconds):
+    """The oracle as it stands, on whole decode steps of the same workload,
+    repeated until `seconds` have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    rows_done, t0 = 0, time.perf_counter()
+    rs = np.arange(c.rows)
+    while True:
+        _, cand = oracle.topk_select(c.logits[:, rs], c.row_starts[rs], c.row_ends[rs], c.ctx,
+                                     c.k, c.S, c.I)
+        ids = oracle.merge_candidates(cand, c.k)
+        slots, counts = oracle.convert_index(ids, c.row_req[rs], c.block_table, 64, c.S, c.I)
+        po, pl = oracle.sparse_mla_partial(c.q[rs], c.cache, c.cache_dtype, c.cache_scale, slots,
+                                           counts, c.sm_scale)
+        oracle.lse_combine(po, pl)
+        rows_done += len(rs)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows_done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done // c.rows} whole steps of the {c.spec.name} workload "
+                      f"({rows_done} rows, full path), float64 NumPy, {el:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build emulates every "
+              "shard on a single MI355X; multi-GPU sharding is a design note, not a benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import dsa_inputs
+    from sparse_attention_indexer_topk_amd.pipeline import DecodePath
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    c = dsa_inputs.make(a.workload)
+    arrays = dsa_inputs.device_arrays(c, device=dev)
+    path = DecodePath(**arrays)
+    logits_sets, q_sets = [path.logits], [path.q]
+    for s in range(1, a.sets):
+        lg, qq = dsa_inputs.redraw_logits_q(c, s)
+        logits_sets.append(torch.from_numpy(lg).to(dev))
+        q_sets.append(torch.from_numpy(qq.view(np.int16)).to(dev).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        j = i % a.sets
+        if ev is not None: ev[0].record(stream)
+        if path.prologue is not None:
+            path.run_prologue()
+        if ev is not None: ev[1].record(stream)
+        path.run_topk(logits=logits_sets[j])
+        if ev is not None: ev[2].record(stream)
+        path.run_merge()
+        if ev is not None: ev[3].record(stream)
+        path.run_convert()
+        if ev is not None: ev[4].record(stream)
+        path.run_attention(q=q_sets[j])
+        if ev is not None: ev[5].record(stream)
+        path.run_combine()
+        if ev is not None: ev[6].record(stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    names = ["fused_rmsnorm_rope", "topk_select", "merge_candidates", "convert_index",
+             "sparse_mla_decode", "lse_combine"]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    kern_us = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            kern_us[n] += ev[j].elapsed_time(ev[j + 1]) * 1e3 / a.steps
+    if path.prologue is None:
+        kern_us.pop("fused_rmsnorm_rope")
+
+    # algorithmic traffic of the last set's step (all sets have the same shape)
+    counts_total = int(path.counts.sum().item())
+    n_valid = 0
+    for i in range(c.rows):
+        n_valid += int(c.row_ends[i]) - int(c.row_starts[i])
+    att_bytes, att_flops = attention_traffic(c, counts_total)
+    tk_bytes, mg_bytes = topk_traffic(c, n_valid)
+    t_att = kern_us["sparse_mla_decode"] * 1e-6
+    att_gbs = att_bytes / t_att / 1e9
+    att_tflops = att_flops / t_att / 1e12
+    bound = "hbm" if att_bytes / (HBM_PEAK_GBS * 1e9) >= att_flops / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "sparse_mla_decode"
+    roof["algorithmic_bytes"] = att_bytes
+    roof["algorithmic_flops"] = att_flops
+    roof["mfma_tflops"] = round(att_tflops, 1)
+
+    t_topk = (kern_us["topk_select"] + kern_us["merge_candidates"]) * 1e-6
+    t_dec = (kern_us["convert_index"] + kern_us["sparse_mla_decode"] + kern_us["lse_combine"]) * 1e-6
+    value = c.rows / (ms_per_step * 1e-3)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.spec.name, "rows": c.rows, "ctx": c.ctx, "k": c.k,
+                   "shards": c.S, "interleave": c.I, "heads": c.heads, "cache": c.cache_dtype,
+                   "input_sets": a.sets},
+        "topk_rows_per_s": round(c.rows / t_topk, 1),
+        "decode_tokens_per_s": round(c.rows / t_dec, 1),
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "topk_merge_hbm_frac": round((tk_bytes + mg_bytes) / (HBM_PEAK_GBS * 1e9) / t_topk, 4),
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(c, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -360,3 +360,48 @@ def make(name_or_spec, *, with_cache: bool = True) -> Case:
             slots[t] = int(blk) * BLOCK + int(loc % BLOCK)
         case.slot_mapping = slots
     return case
+
+
+# --------------------------------------------------------------------------
+# Upload (storage only): the same bits as the host arrays, as device tensors
+# --------------------------------------------------------------------------
+def device_arrays(case: Case, device="cuda", logits=None, q=None) -> dict:
+    """Device copies of a case's inputs, keyed like the decode path's
+    constructor arguments.  bf16 arrays become torch.bfloat16 tensors with
+    identical bits; fp8 codes stay uint8."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    sp = case.spec
+    d = dict(
+        logits=dev(case.logits if logits is None else logits),
+        row_starts=dev(case.row_starts), row_ends=dev(case.row_ends),
+        ctx=sp.ctx, k=sp.k, num_shards=sp.shards, interleave=sp.interleave,
+        q=bf16(case.q if q is None else q),
+        cache=dev(case.cache) if sp.cache == "fp8" else bf16(case.cache),
+        cache_scale=dev(np.array([case.cache_scale], dtype=np.float32)) if sp.cache == "fp8" else None,
+        block_table=dev(case.block_table),
+        row_req=dev(case.row_req), sm_scale=float(case.sm_scale), block_size=BLOCK,
+    )
+    if sp.prologue:
+        d["prologue"] = dict(kv_c=bf16(case.kv_c), k_pe=bf16(case.k_pe), rms_w=bf16(case.rms_w),
+                             eps=float(case.rms_eps), cos_sin=dev(case.cos_sin),
+                             positions=dev(case.positions), slot_mapping=dev(case.slot_mapping))
+    return d
+
+
+def redraw_logits_q(case: Case, index: int):
+    """Another draw of the logits (shard-major) and q of a workload, from an
+    independent seed; the cache, tables and row bounds stay the case's own.
+    Used to rotate several input sets through a benchmark so that a step's
+    inputs are not left in the on-chip caches by the previous step."""
+    sp = case.spec
+    rng = np.random.Generator(np.random.PCG64([sp.seed, 1000 + index]))
+    g = _draw_logits(sp, rng, case.row_starts, case.row_ends)
+    q = _draw_bf16_normal(rng, case.q.shape, 1.0)
+    return shard_layout(g, sp.shards, sp.interleave, SENTINEL), q

@@ -1,0 +1,64 @@
+// LSE-weighted combine of per-shard partial attention outputs.
+//
+// What is computed (PR #52046 report, 关键源码片段: `dcp_manager.combine(
+// attn_out, lse, ...)` merges the shards' partials; PR #46076 report,
+// 评论区精华: the reducer works in base e):
+//   lse = ln sum_p exp(lse_p) over finite lse_p, out = sum_p exp(lse_p - lse) out_p.
+// A (row, head) whose partials are all empty gets out = 0, lse = -inf.
+//
+// How: a pure streaming kernel — one thread per (row, head, 8 features),
+// 16-byte loads of every partial, fp32 accumulation, 16-byte bf16 store.
+#include "launchers.h"
+
+namespace dsa {
+
+constexpr int kCombineThreads = 256;
+constexpr float kLog2eC = 1.4426950408889634f;
+
+__global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
+    const uint16_t* __restrict__ pout, const float* __restrict__ plse, int P, int64_t rh_total,
+    int dim, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  const int chunks = dim / 8;
+  const int64_t gid = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  if (gid >= rh_total * chunks) return;
+  const int64_t rh = gid / chunks;
+  const int c = (int)(gid % chunks);
+
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, plse[(int64_t)p * rh_total + rh]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  if (M != -INFINITY) {
+    for (int p = 0; p < P; ++p) {
+      const float l = plse[(int64_t)p * rh_total + rh];
+      const float w = exp2f((l - M) * kLog2eC);  // exp(-inf) = 0
+      z += w;
+      if (w == 0.f) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
+      const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc[e] += w * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+    }
+  }
+  const float inv = z > 0.f ? 1.0f / z : 0.f;
+  const uint4 o = make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                             pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                             pack_bf16x2(acc[4] * inv, acc[5] * inv),
+                             pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  *reinterpret_cast<uint4*>(out + rh * dim + c * 8) = o;
+  if (lse_out && c == 0) lse_out[rh] = (M == -INFINITY) ? -INFINITY : M + logf(z);
+}
+
+int launch_lse_combine(const void* part_out, const float* part_lse, int P, int rows, int heads,
+                       int dim, void* out, float* lse_out, hipStream_t stream) {
+  const int64_t rh = (int64_t)rows * heads;
+  const int64_t threads = rh * (dim / 8);
+  const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
+                     stream, reinterpret_cast<const uint16_t*>(part_out), part_lse, P, rh, dim,
+                     reinterpret_cast<uint16_t*>(out), lse_out);
+  return 0;
+}
+
+}  // namespace dsa

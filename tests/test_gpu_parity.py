@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* every small parity case, element by element at every stage (prologue,
+  top-K + candidates, merge, convert, partial attention, combine);
+* the five full-size workloads in the launch configuration the benchmark
+  times, on sampled rows the oracle computes one by one;
+* determinism: two runs are bit-identical.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs
+import oracle
+from dsa_testlib import attn_mismatch, bf16_ulp_diff, bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sparse_attention_indexer_topk_amd as dsa  # noqa: E402
+from sparse_attention_indexer_topk_amd.pipeline import DecodePath  # noqa: E402
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cache_bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
+    return bits16(t)
+
+
+def check_prologue(c, path):
+    """Materialised rows within 1 bf16 ulp; inserted bytes exact w.r.t. the
+    GPU's own materialised rows.  Returns the oracle's own inserted rows."""
+    path.run_prologue()
+    torch.cuda.synchronize()
+    kvo, peo = bits16(path.kv_c_out), bits16(path.k_pe_out)
+    okv, ope = oracle.rmsnorm_rope(c.kv_c, c.k_pe, c.rms_w, c.rms_eps, c.cos_sin, c.positions)
+    assert bf16_ulp_diff(kvo, okv).max() <= 1
+    assert bf16_ulp_diff(peo, ope).max() <= 1
+    T = len(c.slot_mapping)
+    sm = torch.from_numpy(c.slot_mapping).to(path.cache.device)
+    g_rows = cache_bits(path.cache.view(-1, 576)[sm])
+    blank = np.zeros((T, 576), dtype=g_rows.dtype)
+    exp_rows = oracle.cache_insert(blank, np.arange(T), kvo, peo, c.cache_dtype, c.cache_scale)
+    assert np.array_equal(g_rows, exp_rows), "inserted cache bytes differ"
+    return oracle.cache_insert(blank, np.arange(T), okv, ope, c.cache_dtype, c.cache_scale)
+
+
+def host_cache_after_insert(c, rows_oracle):
+    flat = c.cache.reshape(-1, 576).copy()
+    flat[c.slot_mapping] = rows_oracle
+    return flat.reshape(c.cache.shape)
+
+
+@pytest.mark.parametrize("name", list(dsa_inputs.PARITY_CASES))
+def test_path_matches_oracle_every_stage(name):
+    log(f"[parity] case {name}")
+    c = dsa_inputs.make(name)
+    path = DecodePath(**dsa_inputs.device_arrays(c))
+    cache_ref = c.cache
+    if c.spec.prologue:
+        rows_oracle = check_prologue(c, path)
+        cache_ref = host_cache_after_insert(c, rows_oracle)
+        # nothing else in the cache moved
+        g = cache_bits(path.cache).reshape(-1, 576)
+        untouched = np.ones(g.shape[0], bool)
+        untouched[c.slot_mapping] = False
+        assert np.array_equal(g[untouched], c.cache.reshape(-1, 576)[untouched])
+
+    path.run_topk(with_local_idx=True)
+    torch.cuda.synchronize()
+    oidx, ocand = oracle.topk_select(c.logits, c.row_starts, c.row_ends, c.ctx, c.k, c.S, c.I)
+    assert np.array_equal(path.local_idx.cpu().numpy(), oidx)
+    assert np.array_equal(path.cand.cpu().numpy().view(np.uint32), ocand.view(np.uint32))
+
+    path.run_merge()
+    torch.cuda.synchronize()
+    oids = oracle.merge_candidates(ocand, c.k)
+    gids = path.ids.cpu().numpy()
+    assert np.array_equal(gids, oids)
+    for i in range(c.rows):   # sharded-then-merged == unsharded
+        e = oracle.unsharded_topk(c.global_logits[i], c.row_starts[i], c.row_ends[i], c.k)
+        assert gids[i, :len(e)].tolist() == e.tolist()
+
+    path.run_convert()
+    torch.cuda.synchronize()
+    oslots, ocounts = oracle.convert_index(oids, c.row_req, c.block_table, 64, c.S, c.I)
+    assert np.array_equal(path.slots.cpu().numpy(), oslots)
+    assert np.array_equal(path.counts.cpu().numpy(), ocounts)
+
+    path.run_attention()
+    torch.cuda.synchronize()
+    opo, opl = oracle.sparse_mla_partial(c.q, cache_ref, c.cache_dtype, c.cache_scale, oslots,
+                                         ocounts, c.sm_scale)
+    gpo = bf16_bits_to_f64(bits16(path.pout))
+    gpl = path.plse.cpu().numpy()
+    bad = attn_mismatch(gpo, opo, gpl, opl)
+    assert not bad, f"partials: {bad}"
+    empty = ocounts == 0
+    if empty.any():   # empty shards still emit (0, -inf)
+        assert np.all(gpo[empty] == 0) and np.all(np.isneginf(gpl[empty]))
+
+    path.run_combine()
+    torch.cuda.synchronize()
+    oo, ol = oracle.lse_combine(opo, opl)
+    bad = attn_mismatch(bf16_bits_to_f64(bits16(path.out)), oo, path.lse.cpu().numpy(), ol)
+    assert not bad, f"combined: {bad}"
+
+
+def sample_rows(name, R):
+    if name == "prefill":
+        picks = [0, 1, 2, 3, 63, 511, 2046, 2047, 2048, 2049, 4095, 6000, 8190, 8191]
+    else:
+        picks = [0, 1, R // 2, R - 1]
+    rng = np.random.default_rng(123)
+    picks += rng.choice(R, min(R, 4), replace=False).tolist()
+    return np.array(sorted({p for p in picks if p < R}), dtype=np.int64)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(dsa_inputs.CONFIGS))
+def test_full_size_workload_sampled_rows(name):
+    log(f"[full] workload {name}: generating")
+    c = dsa_inputs.make(name)
+    path = DecodePath(**dsa_inputs.device_arrays(c))
+    rows_oracle = None
+    if c.spec.prologue:
+        rows_oracle = check_prologue(c, path)
+    log(f"[full] workload {name}: running the step")
+    path.run_topk()
+    path.run_merge()
+    path.run_convert()
+    path.run_attention()
+    path.run_combine()
+    torch.cuda.synchronize()
+    rs = sample_rows(name, c.rows)
+    log(f"[full] workload {name}: oracle on rows {rs.tolist()}")
+    if rows_oracle is not None:
+        flat = c.cache.reshape(-1, 576)
+        flat[c.slot_mapping] = rows_oracle        # in place: the host copy is ours
+    _, ocand = oracle.topk_select(c.logits[:, rs], c.row_starts[rs], c.row_ends[rs], c.ctx, c.k,
+                                  c.S, c.I)
+    gcand = path.cand[torch.from_numpy(rs).cuda()].cpu().numpy()
+    assert np.array_equal(gcand.view(np.uint32), ocand.view(np.uint32))
+    oids = oracle.merge_candidates(ocand, c.k)
+    assert np.array_equal(path.ids.cpu().numpy()[rs], oids)
+    oslots, ocounts = oracle.convert_index(oids, c.row_req[rs], c.block_table, 64, c.S, c.I)
+    assert np.array_equal(path.slots.cpu().numpy()[:, rs], oslots)
+    assert np.array_equal(path.counts.cpu().numpy()[:, rs], ocounts)
+    opo, opl = oracle.sparse_mla_partial(c.q[rs], c.cache, c.cache_dtype, c.cache_scale, oslots,
+                                         ocounts, c.sm_scale)
+    gpo = bf16_bits_to_f64(bits16(path.pout[:, torch.from_numpy(rs).cuda()]))
+    gpl = path.plse.cpu().numpy()[:, rs]
+    bad = attn_mismatch(gpo, opo, gpl, opl)
+    assert not bad, f"partials: {bad}"
+    oo, ol = oracle.lse_combine(opo, opl)
+    go = bf16_bits_to_f64(bits16(path.out[torch.from_numpy(rs).cuda()]))
+    bad = attn_mismatch(go, oo, path.lse.cpu().numpy()[rs], ol)
+    assert not bad, f"combined: {bad}"
+    log(f"[full] workload {name}: ok")
+
+
+@pytest.mark.parametrize("name", ["decode_s", "odd_s", "fp8_s"])
+def test_two_runs_are_bit_identical(name):
+    c = dsa_inputs.make(name)
+    outs = []
+    for _ in range(2):
+        path = DecodePath(**dsa_inputs.device_arrays(c))
+        path.step(with_local_idx=True)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().clone() for t in (path.local_idx, path.cand, path.ids, path.slots,
+                                              path.counts, path.pout.view(torch.int16),
+                                              path.plse, path.out.view(torch.int16), path.lse)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype.is_floating_point else a,
+                           b.view(torch.uint8) if b.dtype.is_floating_point else b)
+
+
+def test_native_library_is_loaded():
+    import os
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(dsa.LIB_PATH) in maps or dsa.LIB_PATH in maps
