@@ -39,7 +39,22 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (3 times), the reference "
+                        "for scaling the HBM byte counters of a profile")
     return p.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "dispatches": 3}), flush=True)
 
 
 def attention_traffic(c, counts_total):
@@ -94,6 +109,9 @@ def cpu_baseline(c, seconds):
 
 def main():
     a = parse()
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build emulates every "
               "shard on a single MI355X; multi-GPU sharding is a design note, not a benchmark.",

@@ -174,17 +174,23 @@ int dsa_convert_index(const int32_t* ids, int32_t rows, int32_t k,
  * slots        [n_parts][rows][k] int32; counts [n_parts][rows] int32 (NULL:
  *              every entry up to k is examined).  Slots outside
  *              [0, num_slots) are skipped.
- * out          [n_parts][rows][heads][512] bf16 output.
- * lse          [n_parts][rows][heads] fp32 output.
+ * splits       split-K factor >= 1: each part's slot list is cut into
+ *              `splits` consecutive pieces (multiples of 32 slots), each
+ *              producing its own partial; partial p*splits + s belongs to
+ *              part p.  All partials merge with dsa_lse_combine.
+ * out          [n_parts*splits][rows][heads][512] bf16 output.
+ * lse          [n_parts*splits][rows][heads] fp32 output.
  * Errors: INVALID_ARG (null pointers, heads not a positive multiple of 16,
- * sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache not bf16/fp8).
+ * splits outside [1, 64], sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache
+ * not bf16/fp8).
  */
 int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads,
                           const void* cache, int32_t cache_dtype,
                           const float* cache_scale, int64_t num_slots,
                           const int32_t* slots, const int32_t* counts,
-                          int32_t k, int32_t n_parts, float sm_scale,
-                          void* out, float* lse, hipStream_t stream);
+                          int32_t k, int32_t n_parts, int32_t splits,
+                          float sm_scale, void* out, float* lse,
+                          hipStream_t stream);
 
 /*
  * dsa_lse_combine — LSE-weighted merge of per-shard partial attention.

@@ -39,8 +39,8 @@ SIGNATURES = {
     "dsa_merge_candidates": [_P, _I32, _I32, _I32, _I32, _P, _P],
     "dsa_convert_index": [_P, _I32, _I32, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
                           _P, _P, _P],
-    "dsa_sparse_mla_decode": [_P, _I32, _I32, _P, _I32, _P, _I64, _P, _P, _I32, _I32, _F32, _P, _P,
-                              _P],
+    "dsa_sparse_mla_decode": [_P, _I32, _I32, _P, _I32, _P, _I64, _P, _P, _I32, _I32, _I32, _F32,
+                              _P, _P, _P],
     "dsa_lse_combine": [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
     "dsa_fused_rmsnorm_rope": [_P, _I64, _P, _I64, _I32, _P, _F32, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                _P, _I64, _P],
@@ -184,13 +184,14 @@ def convert_index(ids: torch.Tensor, block_table: torch.Tensor, *, block_size: i
 
 
 def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
-                      counts: Optional[torch.Tensor], *, sm_scale: float,
+                      counts: Optional[torch.Tensor], *, sm_scale: float, splits: int = 1,
                       cache_scale: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       stream=None):
     """q [rows][heads][576] bf16; cache [...][576] bf16 or uint8 (fp8 e4m3 codes);
-    slots [n_parts][rows][k]; returns out [n_parts][rows][heads][512] bf16 and
-    lse [n_parts][rows][heads] fp32."""
+    slots [n_parts][rows][k]; returns out [n_parts*splits][rows][heads][512]
+    bf16 and lse [n_parts*splits][rows][heads] fp32 (split-K partials of part p
+    are p*splits .. p*splits + splits - 1)."""
     _bits16(q, "q")
     _need(cache, "cache")
     _need(slots, "slots", torch.int32)
@@ -210,14 +211,16 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
     if counts is not None:
         _need(counts, "counts", torch.int32)
     if out is None:
-        out = torch.empty((n_parts, rows, heads, 512), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((n_parts * splits, rows, heads, 512), dtype=torch.bfloat16,
+                          device=q.device)
     if lse is None:
-        lse = torch.empty((n_parts, rows, heads), dtype=torch.float32, device=q.device)
+        lse = torch.empty((n_parts * splits, rows, heads), dtype=torch.float32, device=q.device)
     _bits16(out, "out")
     _need(lse, "lse", torch.float32)
     _check(lib().dsa_sparse_mla_decode(
         _ptr(q), rows, heads, _ptr(cache), cdt, _ptr(cache_scale), num_slots, _ptr(slots),
-        _ptr(counts), k, n_parts, float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+        _ptr(counts), k, n_parts, int(splits), float(sm_scale), _ptr(out), _ptr(lse),
+        _stream(stream)))
     return out, lse
 
 

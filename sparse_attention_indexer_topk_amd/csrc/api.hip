@@ -117,8 +117,8 @@ int dsa_convert_index(const int32_t* ids, int32_t rows, int32_t k, const int32_t
 int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void* cache,
                           int32_t cache_dtype, const float* cache_scale, int64_t num_slots,
                           const int32_t* slots, const int32_t* counts, int32_t k,
-                          int32_t n_parts, float sm_scale, void* out, float* lse,
-                          hipStream_t stream) {
+                          int32_t n_parts, int32_t splits, float sm_scale, void* out,
+                          float* lse, hipStream_t stream) {
   const char* fn = "dsa_sparse_mla_decode";
   if (!q || !cache || !slots || !out || !lse)
     return fail(DSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -128,6 +128,9 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void
   if (!k_ok(k)) return fail(DSA_ERR_UNSUPPORTED_K, "%s: k=%d not in {512, 1024, 2048}", fn, k);
   if (n_parts < 1 || n_parts > 65535)
     return fail(DSA_ERR_INVALID_ARG, "%s: n_parts=%d outside [1, 65535]", fn, n_parts);
+  if (splits < 1 || splits > 64 || (int64_t)n_parts * splits > 65535)
+    return fail(DSA_ERR_INVALID_ARG, "%s: splits=%d outside [1, 64] (or n_parts*splits > 65535)",
+                fn, splits);
   if (cache_dtype != DSA_BF16 && cache_dtype != DSA_FP8_E4M3)
     return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: cache dtype %d is not bf16 or fp8 e4m3", fn,
                 cache_dtype);
@@ -139,7 +142,8 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void
     return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer (q, cache, out need 16 bytes)", fn);
   if (rows == 0) return DSA_OK;
   dsa::launch_sparse_mla_decode(q, rows, heads, cache, cache_dtype == DSA_FP8_E4M3, cache_scale,
-                                num_slots, slots, counts, k, n_parts, sm_scale, out, lse, stream);
+                                num_slots, slots, counts, k, n_parts, splits, sm_scale, out, lse,
+                                stream);
   return launched(fn);
 }
 

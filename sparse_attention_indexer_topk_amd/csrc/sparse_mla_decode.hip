@@ -2,278 +2,406 @@
 // rows of one shard, returning the partial output and a base-e LSE.
 //
 // What is computed (PR #52046 report, 关键源码片段: `forward_mqa(q, kv_cache,
-// ...) -> (attn_out, lse)`, the cache entry being kv_c (512) followed by the
+// ...) -> (attn_out, lse)`, a cache entry being kv_c (512) followed by the
 // roped k_pe (64); PR #46076 report, 实现拆解 item 5 / 评论区精华: the DCP
 // reducer needs the LSE in base e):
 //   s_j = sm_scale * q . K_j (576 wide), out = softmax(s) V, V_j = K_j[0:512],
 //   lse = ln sum_j exp(s_j).
 //
-// How (gfx950):
-//  - a workgroup = 4 waves = 64 heads of one (shard, row); each wave owns 16
-//    heads, holds their q as MFMA B-operand fragments in VGPRs (72 regs) and
-//    their output (512 x 16, fp32) in 32 MFMA accumulators;
-//  - the selected latent rows are gathered 32 tokens at a time from the paged
-//    pool into LDS (row-major for the score product, and the first 512 columns
-//    also transposed, token-contiguous, for the value product), prefetched one
-//    tile ahead in registers;
-//  - scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32_bf16: the accumulator layout then gives each lane 8
-//    tokens of ONE head, exactly the B-operand fragment the value product
-//    O^T += V^T P^T needs — no cross-lane shuffle of P;
-//  - online softmax in base 2 (v_exp_f32 is 2^x): scores are pre-scaled by
-//    log2(e); the final lse is (m + log2 l) * ln 2;
-//  - fp8 e4m3 entries are widened to bf16 exactly (e4m3 is a subset of bf16)
-//    and the per-tensor scale is folded into the score scale and the output.
+// How (gfx950, one workgroup = 8 waves = 128 heads of one (row, part, split)):
+//  - waves work in pairs; a pair owns 32 heads.  Member u of a pair computes
+//    the partial scores over features [288u, 288u + 288) with q in VGPRs as
+//    the B operand of v_mfma_f32_32x32x16_bf16 (18 k-steps, 72 VGPRs); the
+//    pair swaps its fp32 partials through LDS so both hold the full scores,
+//    then member u accumulates output features [256u, 256u + 256) (8 blocks
+//    of 32 x 32 fp32 = 128 accumulators).  That keeps a wave under 256
+//    registers (two waves per SIMD) while the key tile enters LDS once for
+//    all 128 heads;
+//  - the part's slot list is staged once in LDS; the selected latent rows are
+//    gathered 32 tokens per tile straight from HBM into LDS with
+//    global_load_lds_dwordx4 (no register staging) through a 3-stage ring, so
+//    two tiles are in flight while one is consumed; 16-byte chunks of a row
+//    are XOR-swizzled by (token & 7) so the 32 rows one MFMA operand read
+//    touches fall in distinct LDS banks;
+//  - scores are computed transposed, S^T = K Q^T (rows = tokens), so the
+//    accumulator gives each lane 16 tokens of ONE head — exactly the B
+//    operand (P^T) of the value product O^T += V^T P^T;
+//  - V^T fragments are read from the same row-major tile with
+//    ds_read_b64_tr_b16 (LDS transpose read): no transposed copy of V;
+//  - softmax in base 2 (v_exp_f32 computes 2^x) against a reference max
+//    fixed by the first tile: probabilities may exceed 1 by up to 2^64, which
+//    fp32 accumulators and bf16 operands hold exactly as well as values near
+//    1, so the accumulators never need rescaling inside the loop.  A tile
+//    whose max exceeds the reference by more than 2^64 (possible only for
+//    extreme score ranges) restarts the workgroup's token list with the
+//    raised reference — exact, and free of accumulator-wide VALU work in the
+//    hot loop; the denominator sums fp32 probabilities; lse = (m + log2 l) ln 2;
+//  - fp8 e4m3 caches are gathered raw (576 B/row) and widened to bf16 in LDS
+//    with the hardware converter (exact: e4m3 is a subset of bf16); the
+//    per-tensor scale is folded into the score scale and the output;
+//  - split-K: `splits` workgroups share a part's token list, each emitting its
+//    own partial; lse_combine merges them like shards.
 #include "launchers.h"
 
 namespace dsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 
-constexpr int kAttnThreads = 256;
-constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerBlock = 64;
-constexpr int kTile = 32;                 // tokens per LDS tile
-constexpr int kKStride = kLatent + 8;     // bf16 elements per key row in LDS
-constexpr int kVtStride = kTile + 8;      // bf16 elements per transposed value row
-constexpr int kQSteps = kLatent / 32;     // 18 MFMA k-steps over 576
-constexpr int kOBlocks = kValue / 16;     // 32 accumulator blocks of 16 features
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / kWave;   // 8
+constexpr int kHPW = 32;                       // heads per wave pair
+constexpr int kHPB = kHPW * kAttnWaves / 2;    // heads per block (128)
+constexpr int kTile = 32;                      // tokens per tile
+constexpr int kStages = 3;                     // tiles in the LDS ring
+constexpr int kRowB = kLatent * 2;             // bf16 row bytes (1152)
+constexpr int kRowChunks = kRowB / 16;         // 72 16-byte chunks
+constexpr int kTileB = kTile * kRowB;          // 36864 bytes
+constexpr int kRowB8 = kLatent;                // fp8 row bytes (576)
+constexpr int kTileB8 = kTile * kRowB8;        // 18432 bytes
+constexpr int kQSteps = kLatent / 16 / 2;      // 18 per pair member
+constexpr int kOBlocks = kValue / 32 / 2;      // 8 per pair member
+constexpr int kMaxSel = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRestartSlack = 64.0f;         // log2 units
 
-// e4m3 code (low byte) -> bf16 bits, exact.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t b) {
-  const uint32_t s = (b & 0x80u) << 8;
-  const uint32_t em = b & 0x7fu;
-  if (em == 0x7fu) return s | 0x7fc0u;                      // NaN
-  const uint32_t e = em >> 3, m = em & 7u;
-  if (e) return s | ((e + 120u) << 7) | (m << 4);
-  if (m == 0) return s;
-  const float f = (float)m * 0.001953125f;                  // m * 2^-9, exact
-  return s | (__float_as_uint(f) >> 16);
+// DMA instructions (64 lanes x 16 B) per tile, dealt round-robin to the waves
+constexpr int kDmaBf16Total = kTileB / (16 * kWave);           // 36
+constexpr int kDmaFp8Total = kTileB8 / (16 * kWave);           // 18
+
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void lgkm_wait0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+// byte offset of logical 16-byte chunk c of token row t inside a bf16 tile
+__device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ (t & 7)) << 4); }
 
 template <bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 1) void sparse_mla_decode_kernel(
-    const uint16_t* __restrict__ q, int rows, int heads, const void* __restrict__ cache,
+__global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
+    const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
     const float* __restrict__ cache_scale, int64_t num_slots, const int* __restrict__ slots,
-    const int* __restrict__ counts, int k, float sm_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kValue * kVtStride];
-  __shared__ int s_slot[2][kTile];
+    const int* __restrict__ counts, int k, int splits, float sm_scale,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kRingB = FP8 ? kTileB8 : kTileB;
+  constexpr int kDmaTotal = FP8 ? kDmaFp8Total : kDmaBf16Total;
+  constexpr int kDmaMax = (kDmaTotal + kAttnWaves - 1) / kAttnWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kStages][kRingB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_conv[FP8 ? kTileB : 16];
+  __shared__ __attribute__((aligned(16))) float4 s_x[kAttnWaves][4][kWave];  // score partials
+  __shared__ int s_slot[kMaxSel];
+  __shared__ int s_restart;
 
-  // x = row, y = part, z = head group: the head groups of one (row, part)
-  // read the same latent rows and sit rows*parts workgroup ids apart, which
-  // keeps them on one XCD (and its L2) when rows*parts is a multiple of 8.
   const int row = blockIdx.x;
-  const int part = blockIdx.y;
+  const int part = blockIdx.y / splits;
+  const int split = blockIdx.y % splits;
   const int hg = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int pair = wave >> 1;
+  const int u = wave & 1;         // pair member: feature half
   const int lane = lane_id();
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;
-  const int h0 = hg * kHeadsPerBlock + wave * kHeadsPerWave;
-  const bool active = h0 < heads;
+  const int j32 = lane & 31;      // head column / token row of 32x32 operands
+  const int g = lane >> 5;        // k-group of 32x32 operands
+  const int h0 = hg * kHPB + pair * kHPW;
+  const int head = h0 + j32;
+  const bool pair_on = h0 < heads;
+  const bool head_on = head < heads;
+  const int out_part = blockIdx.y;
 
-  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
+  // ---- this split's slice of the part's token list --------------------------
   int cnt = counts ? counts[(int64_t)part * rows + row] : k;
   cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
+  if (num_slots <= 0) cnt = 0;
+  const int per = ((cnt + splits - 1) / splits + kTile - 1) / kTile * kTile;
+  const int t_lo = split * per < cnt ? split * per : cnt;
+  const int t_hi = t_lo + per < cnt ? t_lo + per : cnt;
+  const int n_tok = t_hi - t_lo;
+  const int ntiles = (n_tok + kTile - 1) / kTile;
+
+  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
+  for (int i = tid; i < n_tok; i += kAttnThreads) {
+    const int s = my_slots[t_lo + i];
+    s_slot[i] = (s < 0 || (int64_t)s >= num_slots) ? -1 : s;
+  }
+
   const float kv_scale = FP8 ? cache_scale[0] : 1.0f;
   const float qk_scale = sm_scale * kv_scale * kLog2e;
 
-  // q fragments (B operand of S^T = K Q^T): head h0 + l16, features
-  // 32*kk + 8*grp .. +8
+  // q fragments: head `head`, features 288*u + 16*kk + 8*g .. +8
   bf16x8_t qf[kQSteps];
-  if (active) {
-    const uint16_t* qp = q + ((int64_t)row * heads + h0 + l16) * kLatent + 8 * grp;
+  {
+    const uint16_t* qp =
+        q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 288 * u + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kk);
+    for (int kk = 0; kk < kQSteps; ++kk) {
+      u16x8_t v = *reinterpret_cast<const u16x8_t*>(qp + 16 * kk);
+      if (!head_on) v = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  f32x16_t o[kOBlocks];
+#pragma unroll
+  for (int mb = 0; mb < kOBlocks; ++mb)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+  float m_ref = -INFINITY, l_part = 0.f;
+  if (tid == 0) s_restart = 0;
+  __syncthreads();   // slot list and flag ready
+
+  // ---- lane-invariant LDS byte offsets inside a bf16 tile -------------------
+  // scores: k-step kk of member u reads logical chunk 36u + g + 2kk of token
+  // row j32 -> qk_off[kk % 4] + 128 * (kk / 4)
+  int qk_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qk_off[i] = chunk_off(j32, 36 * u + g + 2 * i);
+  // values (transpose reads): 16-lane group G = lane/16 has k-group g = G/2
+  // and feature half fs = G%2; inside it, source role sp = lane%16 reads
+  // token row 8*(2*ks + h) + 4*g + sp/4 at features
+  // 256u + 32mb + 16fs + 4(sp%4) -> pv_off[mb % 2] + 8*(2ks+h)*row + 128*(mb/2)
+  int pv_off[2];
+  {
+    const int sp = lane & 15, fs = (lane >> 4) & 1;
+    const int trb = 4 * g + (sp >> 2);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int feat = 256 * u + 32 * par + 16 * fs + 4 * (sp & 3);
+      pv_off[par] = chunk_off(trb, feat >> 3) + (feat & 7) * 2;
+    }
   }
 
-  f32x4_t o[kOBlocks];
+  // ---- DMA issue of tile tt into its ring stage -------------------------------
+  // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
+  // instructions are dealt round-robin to the waves.
+  auto issue = [&](int tt) {
+    uint8_t* stage = s_ring[tt % kStages];
+    const int tbase = tt * kTile;
 #pragma unroll
-  for (int mb = 0; mb < kOBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // ---- gather plumbing ----------------------------------------------------
-  // bf16: a tile is 32 rows x 72 16-byte chunks = 2304 chunks, 9 per thread.
-  // fp8 : 32 rows x 36 16-byte chunks (16 codes each) = 1152, 4.5 per thread.
-  constexpr int kChunksPerRow = FP8 ? kLatent / 16 : kLatent / 8;
-  constexpr int kChunks = kTile * kChunksPerRow;
-  constexpr int kPerThread = (kChunks + kAttnThreads - 1) / kAttnThreads;
-  uint4 pre[kPerThread];
-  const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(cache);
-  const uint16_t* cache16 = reinterpret_cast<const uint16_t*>(cache);
-
-  auto load_slots = [&](int t0, int buf) {
-    if (tid < kTile) {
-      const int t = t0 + tid;
-      int s = -1;
-      if (t < cnt) {
-        s = my_slots[t];
-        if (s < 0 || (int64_t)s >= num_slots) s = -1;
-      }
-      s_slot[buf][tid] = s;
-    }
-  };
-  auto fetch = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < kPerThread; ++it) {
-      const int c = it * kAttnThreads + tid;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < kChunks) {
-        const int tok = c / kChunksPerRow;
-        const int piece = c % kChunksPerRow;
-        const int s = s_slot[buf][tok];
-        if (s >= 0) {
-          if constexpr (FP8)
-            v = *reinterpret_cast<const uint4*>(cache8 + (int64_t)s * kLatent + piece * 16);
-          else
-            v = *reinterpret_cast<const uint4*>(cache16 + (int64_t)s * kLatent + piece * 8);
+    for (int jj = 0; jj < kDmaMax; ++jj) {
+      const int ins = jj * kAttnWaves + wave;
+      if (ins < kDmaTotal) {
+        int p = ins * kWave + lane;
+        asm volatile("" : "+v"(p));   // recompute per issue: keep it out of loop-invariant VGPRs
+        int t, off;
+        if constexpr (FP8) {
+          t = p / (kRowB8 / 16);                       // raw rows, unswizzled
+          off = (p % (kRowB8 / 16)) * 16;
+        } else {
+          t = p / kRowChunks;                          // chunk slot -> logical chunk
+          off = ((p % kRowChunks) ^ (t & 7)) * 16;
         }
-      }
-      pre[it] = v;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < kPerThread; ++it) {
-      const int c = it * kAttnThreads + tid;
-      if (c >= kChunks) break;
-      const int tok = c / kChunksPerRow;
-      const int piece = c % kChunksPerRow;
-      if constexpr (FP8) {
-        const uint32_t w[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
-        uint32_t h[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) h[e] = e4m3_to_bf16_bits((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
-        uint4 lo4 = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                               h[6] | (h[7] << 16));
-        uint4 hi4 = make_uint4(h[8] | (h[9] << 16), h[10] | (h[11] << 16),
-                               h[12] | (h[13] << 16), h[14] | (h[15] << 16));
-        uint16_t* dst = s_k + tok * kKStride + piece * 16;
-        *reinterpret_cast<uint4*>(dst) = lo4;
-        *reinterpret_cast<uint4*>(dst + 8) = hi4;
-        if (piece * 16 < kValue) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s_vt[(piece * 16 + e) * kVtStride + tok] = (uint16_t)h[e];
-        }
-      } else {
-        *reinterpret_cast<uint4*>(s_k + tok * kKStride + piece * 8) = pre[it];
-        if (piece * 8 < kValue) {
-          const uint32_t w[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            s_vt[(piece * 8 + e) * kVtStride + tok] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        }
+        const int ti = tbase + t < n_tok ? tbase + t : 0;
+        const int s = max(s_slot[ti], 0);              // masked later; any valid row
+        const uint8_t* src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + off;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (lds_void_ptr)(stage + ins * kWave * 16), 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+  // this wave's DMA instructions per tile
+  const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  // ---- main loop over tiles of 32 selected tokens -------------------------
-  if (cnt > 0) {
-    load_slots(0, 0);
-    __syncthreads();
-    fetch(0);
-  }
-  for (int t0 = 0; t0 < cnt; t0 += kTile) {
-    const int buf = (t0 / kTile) & 1;
-    store_tile();
-    __syncthreads();                       // tile in LDS; slot list of buf final
-    const int t_next = t0 + kTile;
-    if (t_next < cnt) load_slots(t_next, buf ^ 1);
-    __syncthreads();
-    if (t_next < cnt) fetch(buf ^ 1);      // overlaps with the math below
+  int next_issue = 0;   // next tile whose DMA has not been issued
+  for (int tt = 0; tt < ntiles;) {
+    // keep two tiles in flight beyond tile tt (fills the ring at the start
+    // and after a restart)
+    while (next_issue < ntiles && next_issue <= tt + 2) issue(next_issue++);
+    // wait for this wave's DMA of tile tt; younger tiles may stay in flight
+    switch ((next_issue - 1 - tt) * my_dma) {
+      case 10: vm_wait<10>(); break;
+      case 9: vm_wait<9>(); break;
+      case 8: vm_wait<8>(); break;
+      case 6: vm_wait<6>(); break;
+      case 5: vm_wait<5>(); break;
+      case 4: vm_wait<4>(); break;
+      case 3: vm_wait<3>(); break;
+      case 2: vm_wait<2>(); break;
+      default: vm_wait<0>(); break;
+    }
+    bar();
 
-    if (active) {
-      // S^T for two 16-token blocks; M-block b row rho <-> tile token
-      // 8*(rho/4) + 4*b + rho%4, so lane (grp) ends up with tokens 8*grp..+8.
-      f32x4_t sacc[2];
+    const uint8_t* tile = s_ring[tt % kStages];
+    if constexpr (FP8) {
+      // widen to the swizzled bf16 layout: 1152 chunks of 16 codes
+      for (int c = tid; c < kTileB8 / 16; c += kAttnThreads) {
+        const int t = c / (kRowB8 / 16);
+        const int c8 = c % (kRowB8 / 16);            // features 16*c8 .. +16
+        const uint4 raw = *reinterpret_cast<const uint4*>(tile + c * 16);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t h[8];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int tok = 8 * (l16 >> 2) + 4 * b + (l16 & 3);
-        const uint16_t* kp = s_k + tok * kKStride + 8 * grp;
-#pragma unroll
-        for (int kk = 0; kk < kQSteps; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kp + 32 * kk);
-          sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[b], 0, 0, 0);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, false);
+          const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, true);
+          h[2 * q4] = __builtin_bit_cast(uint32_t, lo);
+          h[2 * q4 + 1] = __builtin_bit_cast(uint32_t, hi);
         }
+        *reinterpret_cast<uint4*>(s_conv + chunk_off(t, 2 * c8)) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(s_conv + chunk_off(t, 2 * c8 + 1)) =
+            make_uint4(h[4], h[5], h[6], h[7]);
       }
-      // lane holds head h0 + l16, tokens 8*grp + e (e = 4*b + i)
-      float sv[8];
+      lgkm_wait0();
+      bar();
+      tile = s_conv;
+    }
+
+    // token validity of this tile as a wave-uniform bit mask
+    const int tbase = tt * kTile;
+    const uint64_t vmask =
+        __ballot(lane < kTile && tbase + lane < n_tok && s_slot[tbase + (lane & 31)] >= 0);
+
+    // ---- partial S^T = K Q^T over this member's 288 features -----------------
+    f32x16_t sacc;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) sacc[a] = 0.f;
+    if (pair_on) {
+      // k-step kk reads logical chunk c0 + 2*kk of token row j32; the swizzle
+      // only permutes the low 3 chunk bits, so the address is one of 4
+      // per-lane bases (kk % 4) plus 128 bytes per 4 k-steps
+#pragma unroll
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(tile + qk_off[kk & 3] + 128 * (kk >> 2));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+        if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        s_x[wave][a4][lane] = make_float4(sacc[4 * a4], sacc[4 * a4 + 1], sacc[4 * a4 + 2],
+                                          sacc[4 * a4 + 3]);
+    }
+    lgkm_wait0();
+    bar();                                           // partials visible
+    if (pair_on) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 x = s_x[wave ^ 1][a4][lane];
+        sacc[4 * a4] += x.x;
+        sacc[4 * a4 + 1] += x.y;
+        sacc[4 * a4 + 2] += x.z;
+        sacc[4 * a4 + 3] += x.w;
+      }
+      // lane holds head `head`, tokens 8*(a/4) + 4*g + a%4 (same in both members)
+      // this lane's tokens 8*b + 4*g + r: shift the tile mask by 4*g once,
+      // then test the constant bit 8*b + r
+      const uint32_t vm = (uint32_t)(vmask >> (4 * g));
+      float sv[16];
       float mt = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 8 * grp + e;
-        const bool ok = (t0 + tok < cnt) && (s_slot[buf][tok] >= 0);
-        sv[e] = ok ? sacc[e >> 2][e & 3] * qk_scale : -INFINITY;
-        mt = fmaxf(mt, sv[e]);
+      for (int a = 0; a < 16; ++a) {
+        sv[a] = ((vm >> (8 * (a >> 2) + (a & 3))) & 1u) ? sacc[a] * qk_scale : -INFINITY;
+        mt = fmaxf(mt, sv[a]);
       }
-      mt = max_over_groups(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-      u16x8_t pb;
-      float ls = 0.f;
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      if (m_ref == -INFINITY) {
+        m_ref = mt;                        // first tile with a valid token
+      } else if (__any(mt > m_ref + kRestartSlack)) {
+        m_ref = fmaxf(m_ref, mt);          // raise, then restart (below)
+        if (lane == 0) s_restart = 1;
+      }
+      bf16x8_t pf0, pf1;   // probabilities, rounded to nearest even by the hardware
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t b16 = f32_to_bf16(exp2f(sv[e] - base));
-        pb[e] = b16;
-        ls += bf16_to_f32(b16);
+      for (int a = 0; a < 16; ++a) {
+        const float p = (m_ref == -INFINITY) ? 0.f : exp2f(sv[a] - m_ref);
+        l_part += p;
+        if (a < 8) pf0[a] = static_cast<__bf16>(p);
+        else pf1[a - 8] = static_cast<__bf16>(p);
       }
-      ls = sum_over_groups(ls);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pb);
+
+      // ---- O^T += V^T P^T over this member's 256 output features --------------
+      // V^T fragments come from the row-major tile through ds_read_b64_tr_b16:
+      // 16-lane group G = lane/16 has k-group g = G/2 and feature half fs = G%2;
+      // inside it, source role sp = lane%16 addresses token row
+      // 8*(2*ks + h) + 4*g + sp/4 at features f + 16*fs + 4*(sp%4).
+      auto vfrag = [&](int mb, int ks) {
+        s16x4_t v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(
+              tile + pv_off[mb & 1] + 8 * (2 * ks + h) * kRowB + 128 * (mb >> 1)));
+        return __builtin_bit_cast(bf16x8_t,
+                                  __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      };
 #pragma unroll
       for (int mb = 0; mb < kOBlocks; ++mb) {
-        o[mb] *= alpha;
-        const uint16_t* vp = s_vt + (16 * mb + l16) * kVtStride + 8 * grp;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vp);
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[mb], 0, 0, 0);
+        const bf16x8_t va0 = vfrag(mb, 0), va1 = vfrag(mb, 1);
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pf0, o[mb], 0, 0, 0);
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pf1, o[mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();                       // LDS tile free for the next store
+    lgkm_wait0();
+    bar();   // stage tt % 3, s_conv and s_x free again; s_restart final
+    if (s_restart) {
+      // a reference max moved by more than 2^64: drop the partial sums and
+      // replay the token list (every wave, since the tile ring is shared)
+      vm_wait<0>();
+      bar();
+      if (tid == 0) s_restart = 0;
+#pragma unroll
+      for (int mb = 0; mb < kOBlocks; ++mb)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+      l_part = 0.f;
+      __syncthreads();
+      tt = 0;
+      next_issue = 0;
+      continue;
+    }
+    ++tt;
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  if (active) {
-    const float inv = l_run > 0.f ? kv_scale / l_run : 0.f;
-    uint16_t* op = out + (((int64_t)part * rows + row) * heads + h0 + l16) * kValue + 4 * grp;
+  // ---- epilogue ---------------------------------------------------------------
+  if (pair_on) {
+    const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
+    if (head_on) {
+      const float inv = l_tot > 0.f ? kv_scale / l_tot : 0.f;
+      uint16_t* op =
+          out + (((int64_t)out_part * rows + row) * heads + head) * kValue + 256 * u + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < kOBlocks; ++mb) {
-      const uint2 v = make_uint2(pack_bf16x2(o[mb][0] * inv, o[mb][1] * inv),
-                                 pack_bf16x2(o[mb][2] * inv, o[mb][3] * inv));
-      *reinterpret_cast<uint2*>(op + 16 * mb) = v;
-    }
-    if (grp == 0) {
-      const float lv = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-      lse[((int64_t)part * rows + row) * heads + h0 + l16] = lv;
+      for (int mb = 0; mb < kOBlocks; ++mb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint2 v = make_uint2(pack_bf16x2(o[mb][4 * b] * inv, o[mb][4 * b + 1] * inv),
+                                     pack_bf16x2(o[mb][4 * b + 2] * inv, o[mb][4 * b + 3] * inv));
+          *reinterpret_cast<uint2*>(op + 32 * mb + 8 * b) = v;
+        }
+      if (g == 0 && u == 0) {
+        const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+        lse[((int64_t)out_part * rows + row) * heads + head] = lv;
+      }
     }
   }
 }
 
-int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cache,
-                             bool fp8, const float* cache_scale, int64_t num_slots,
-                             const int* slots, const int* counts, int k, int n_parts,
-                             float sm_scale, void* out, float* lse, hipStream_t stream) {
-  dim3 grid(rows, n_parts, (heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cache, bool fp8,
+                             const float* cache_scale, int64_t num_slots, const int* slots,
+                             const int* counts, int k, int n_parts, int splits, float sm_scale,
+                             void* out, float* lse, hipStream_t stream) {
+  dim3 grid(rows, n_parts * splits, (heads + kHPB - 1) / kHPB);
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+  const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cache);
   uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
   if (fp8) {
     hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, dim3(kAttnThreads), 0, stream, q16,
-                       rows, heads, cache, cache_scale, num_slots, slots, counts, k, sm_scale,
+                       rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits, sm_scale,
                        o16, lse);
   } else {
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kAttnThreads), 0, stream,
-                       q16, rows, heads, cache, cache_scale, num_slots, slots, counts, k,
-                       sm_scale, o16, lse);
+    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kAttnThreads), 0, stream, q16,
+                       rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits, sm_scale,
+                       o16, lse);
   }
   return 0;
 }

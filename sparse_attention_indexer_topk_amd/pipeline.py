@@ -42,7 +42,7 @@ class DecodePath:
                  interleave: int, q: torch.Tensor, cache: torch.Tensor,
                  cache_scale: Optional[torch.Tensor], block_table: torch.Tensor,
                  row_req: Optional[torch.Tensor], sm_scale: float, block_size: int = 64,
-                 prologue=None):
+                 prologue=None, splits: Optional[int] = None):
         self.logits, self.row_starts, self.row_ends = logits, row_starts, row_ends
         self.ctx, self.k, self.S, self.I = ctx, k, num_shards, interleave
         self.q, self.cache, self.cache_scale = q, cache, cache_scale
@@ -54,13 +54,17 @@ class DecodePath:
         dev = logits.device
         R, H = q.shape[0], q.shape[1]
         S = num_shards
+        if splits is None:   # enough workgroups to cover the 256 CUs
+            blocks = R * S * ((H + 127) // 128)
+            splits = max(1, min(8, -(-256 // blocks)))
+        self.splits = splits
         self.cand = torch.empty((R, S * k, 2), dtype=torch.float32, device=dev)
         self.local_idx = torch.empty((S, R, k), dtype=torch.int32, device=dev)
         self.ids = torch.empty((R, k), dtype=torch.int32, device=dev)
         self.slots = torch.empty((S, R, k), dtype=torch.int32, device=dev)
         self.counts = torch.empty((S, R), dtype=torch.int32, device=dev)
-        self.pout = torch.empty((S, R, H, 512), dtype=torch.bfloat16, device=dev)
-        self.plse = torch.empty((S, R, H), dtype=torch.float32, device=dev)
+        self.pout = torch.empty((S * splits, R, H, 512), dtype=torch.bfloat16, device=dev)
+        self.plse = torch.empty((S * splits, R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((R, H), dtype=torch.float32, device=dev)
         if prologue is not None:
@@ -92,7 +96,8 @@ class DecodePath:
 
     def run_attention(self, stream=None, q=None):
         sparse_mla_decode(self.q if q is None else q, self.cache, self.slots, self.counts,
-                          sm_scale=self.sm_scale, cache_scale=self.cache_scale, out=self.pout,
+                          sm_scale=self.sm_scale, splits=self.splits,
+                          cache_scale=self.cache_scale, out=self.pout,
                           lse=self.plse, stream=stream)
 
     def run_combine(self, stream=None):

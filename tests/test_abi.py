@@ -103,10 +103,11 @@ def test_sparse_mla_decode_rejects():
     f = L.dsa_sparse_mla_decode
     def call(**kw):
         a = dict(q=FAKE, rows=0, heads=128, cache=FAKE, dt=dsa.DSA_BF16, scale=None, nslots=100,
-                 slots=FAKE, counts=None, k=2048, parts=4, sm=0.04, out=FAKE, lse=FAKE)
+                 slots=FAKE, counts=None, k=2048, parts=4, splits=1, sm=0.04, out=FAKE, lse=FAKE)
         a.update(kw)
         return f(a["q"], a["rows"], a["heads"], a["cache"], a["dt"], a["scale"], a["nslots"],
-                 a["slots"], a["counts"], a["k"], a["parts"], a["sm"], a["out"], a["lse"], None)
+                 a["slots"], a["counts"], a["k"], a["parts"], a["splits"], a["sm"], a["out"],
+                 a["lse"], None)
     assert call() == OK
     assert call(heads=24) == INV
     assert call(heads=0) == INV
@@ -116,6 +117,9 @@ def test_sparse_mla_decode_rejects():
     assert call(dt=dsa.DSA_FP8_E4M3, scale=FAKE) == OK
     assert call(q=FAKE + 8) == INV
     assert call(parts=0) == INV
+    assert call(splits=0) == INV
+    assert call(splits=65) == INV
+    assert call(splits=8) == OK
     assert call(rows=-3) == INV
 
 

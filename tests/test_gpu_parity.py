@@ -99,23 +99,45 @@ def test_path_matches_oracle_every_stage(name):
     assert np.array_equal(path.slots.cpu().numpy(), oslots)
     assert np.array_equal(path.counts.cpu().numpy(), ocounts)
 
-    path.run_attention()
-    torch.cuda.synchronize()
     opo, opl = oracle.sparse_mla_partial(c.q, cache_ref, c.cache_dtype, c.cache_scale, oslots,
                                          ocounts, c.sm_scale)
-    gpo = bf16_bits_to_f64(bits16(path.pout))
-    gpl = path.plse.cpu().numpy()
-    bad = attn_mismatch(gpo, opo, gpl, opl)
-    assert not bad, f"partials: {bad}"
-    empty = ocounts == 0
-    if empty.any():   # empty shards still emit (0, -inf)
-        assert np.all(gpo[empty] == 0) and np.all(np.isneginf(gpl[empty]))
+    oo, ol = oracle.lse_combine(opo, opl)
+    auto_splits = path.splits
+    for splits in sorted({1, auto_splits, 3}):
+        check_attention(c, path, splits, opo, opl, oo, ol, ocounts)
 
+
+def split_partials_to_parts(gpo, gpl, S, splits):
+    """Merge each part's split-K partials (GPU bf16 outputs) with the oracle's
+    own combine, giving one partial per part."""
+    outs, lses = [], []
+    for p in range(S):
+        o, l = oracle.lse_combine(gpo[p * splits:(p + 1) * splits], gpl[p * splits:(p + 1) * splits])
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def check_attention(c, path, splits, opo, opl, oo, ol, ocounts):
+    path.splits = splits
+    S, R, H = c.S, c.rows, c.heads
+    path.pout = torch.empty((S * splits, R, H, 512), dtype=torch.bfloat16, device="cuda")
+    path.plse = torch.empty((S * splits, R, H), dtype=torch.float32, device="cuda")
+    path.run_attention()
+    torch.cuda.synchronize()
+    gpo = bf16_bits_to_f64(bits16(path.pout))
+    gpl = path.plse.cpu().numpy().astype(np.float64)
+    if splits == 1:
+        empty = ocounts == 0
+        if empty.any():   # empty shards still emit (0, -inf)
+            assert np.all(gpo[empty] == 0) and np.all(np.isneginf(gpl[empty]))
+    gpo_p, gpl_p = split_partials_to_parts(gpo, gpl, S, splits)
+    bad = attn_mismatch(gpo_p, opo, gpl_p, opl)
+    assert not bad, f"partials (splits={splits}): {bad}"
     path.run_combine()
     torch.cuda.synchronize()
-    oo, ol = oracle.lse_combine(opo, opl)
     bad = attn_mismatch(bf16_bits_to_f64(bits16(path.out)), oo, path.lse.cpu().numpy(), ol)
-    assert not bad, f"combined: {bad}"
+    assert not bad, f"combined (splits={splits}): {bad}"
 
 
 def sample_rows(name, R):
@@ -162,7 +184,8 @@ def test_full_size_workload_sampled_rows(name):
     opo, opl = oracle.sparse_mla_partial(c.q[rs], c.cache, c.cache_dtype, c.cache_scale, oslots,
                                          ocounts, c.sm_scale)
     gpo = bf16_bits_to_f64(bits16(path.pout[:, torch.from_numpy(rs).cuda()]))
-    gpl = path.plse.cpu().numpy()[:, rs]
+    gpl = path.plse.cpu().numpy()[:, rs].astype(np.float64)
+    gpo, gpl = split_partials_to_parts(gpo, gpl, c.S, path.splits)
     bad = attn_mismatch(gpo, opo, gpl, opl)
     assert not bad, f"partials: {bad}"
     oo, ol = oracle.lse_combine(opo, opl)
