@@ -78,6 +78,28 @@ def topk_traffic(c, n_valid_logits):
     return topk, merge
 
 
+def measured_traffic(workload):
+    """HBM bytes per sparse_mla_decode launch from the committed counter
+    summary, or None when the summary is for another workload or the kernel
+    source changed since the counters were taken."""
+    import hashlib
+    import re
+    if workload != "decode":
+        return None
+    summary = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
+    src = os.path.join(ROOT, "sparse_attention_indexer_topk_amd", "csrc", "sparse_mla_decode.hip")
+    try:
+        text = open(summary).read()
+        m = re.search(r"sparse_mla_decode traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)",
+                      text)
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if not m or m.group(2) != sha:
+        return None
+    return int(m.group(1))
+
+
 def cpu_baseline(c, seconds):
     """The oracle as it stands, on whole decode steps of the same workload,
     repeated until `seconds` have passed."""
@@ -194,7 +216,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(c.spec.name)
     roof["kernel"] = "sparse_mla_decode"
     roof["algorithmic_bytes"] = att_bytes
     roof["algorithmic_flops"] = att_flops
