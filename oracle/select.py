@@ -106,21 +106,30 @@ def convert_index(ids, row_req, block_table, block_size, S, I, first=0, count=No
     ``block_table``: ``[count][Rq][W]`` (slice j = shard ``first + j``);
     ``row_req``: request of each row (None = identity).
     Returns ``slots [count][R][k]`` int32, ``counts [count][R]`` int32.
+
+    Guards the pages leave open (the page's kernel is handed a table that
+    covers every id): a row whose request is outside ``[0, Rq)`` keeps
+    nothing, and an id whose block column is ``>= W`` is dropped.
     """
     count = S - first if count is None else count
     R, k = ids.shape
     slots = np.full((count, R, k), -1, dtype=np.int32)
     counts = np.zeros((count, R), dtype=np.int32)
+    n_req, width = block_table.shape[1], block_table.shape[2]
     for j in range(count):
         r = first + j
         for i in range(R):
             req = i if row_req is None else int(row_req[i])
             out = []
+            if not 0 <= req < n_req:       # no such request: nothing to look up
+                continue
             for g in ids[i]:
                 g = int(g)
                 if g < 0 or int(owner(g, S, I)) != r:
                     continue
                 l = int(local(g, S, I))
+                if l // block_size >= width:  # beyond the table: not a cached token
+                    continue
                 blk = int(block_table[j, req, l // block_size])
                 out.append(blk * block_size + l % block_size)
             slots[j, i, :len(out)] = out

@@ -8,91 +8,98 @@
 // through its block table (slot = block * block_size + offset) and packs the
 // slots at the front, -1 after them.
 //
-// How: one workgroup per row handles every shard of the run.  Ids are read
-// 256 at a time; for each shard a wave ballot marks the lanes whose id the
-// shard owns, the lane's rank among them is a popcount of the lower lanes,
-// and per-wave totals give the block offsets.  The compaction therefore keeps
-// input order deterministically (no atomic slot counter).
+// How: one workgroup of 256 threads per (row, shard).  Thread t owns the E =
+// k/256 contiguous ids [t*E, t*E+E) of the row (every shard's group reads the
+// same ids, from L2 after the first); it resolves the ones its shard owns,
+// a block exclusive scan of the per-thread counts (DPP inside each wave, one
+// barrier across waves) gives every kept slot its position, so compaction
+// keeps input order deterministically (no atomic slot counter).
 #include "launchers.h"
+#include "select_common.h"
 
 namespace dsa {
 
 constexpr int kConvThreads = 256;
 
+template <int E>
 __global__ __launch_bounds__(kConvThreads) void convert_index_kernel(
     const int* __restrict__ ids, int rows, int k, const int* __restrict__ row_req,
     int num_reqs, const int* __restrict__ block_table, int64_t bt_ld, int64_t bt_stride,
-    int bs, int S, int I, int first, int count, int* __restrict__ slots,
-    int* __restrict__ counts) {
+    int bs, int S, int I, int first, int* __restrict__ slots, int* __restrict__ counts,
+    int vec) {
   constexpr int NT = kConvThreads;
-  constexpr int NW = NT / kWave;
-  __shared__ uint32_t s_wave[16][NW];
-  __shared__ uint32_t s_run[16];
+  __shared__ uint32_t s_scan[NT / kWave];
 
   const int row = blockIdx.x;
+  const int j = blockIdx.y;
+  const int r = first + j;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = lane_id();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const int req = row_req ? row_req[row] : row;
   const bool req_ok = req >= 0 && req < num_reqs;
-  const int* my_ids = ids + (int64_t)row * k;
+  const int* my_ids = ids + (int64_t)row * k + tid * E;
+  const int* bt = block_table + (int64_t)j * bt_stride + (int64_t)(req_ok ? req : 0) * bt_ld;
+  int* dst = slots + ((int64_t)j * rows + row) * k;
 
-  if (tid < count) s_run[tid] = 0;
-  __syncthreads();
+  int g[E];
+  if (vec) {
+#pragma unroll
+    for (int v = 0; v < E; v += 2) {
+      const int2 x = *reinterpret_cast<const int2*>(my_ids + v);
+      g[v] = x.x;
+      g[v + 1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) g[e] = my_ids[e];
+  }
 
-  for (int base = 0; base < k; base += NT) {
-    const int i = base + tid;
-    const int g = (i < k && req_ok) ? my_ids[i] : -1;
-    int sh = -1, slot = -1;
-    if (g >= 0) {
-      const int r = owner_of(g, S, I);
-      if (r >= first && r < first + count) {
-        const int l = local_of(g, S, I);
-        const int col = l / bs;
-        if ((int64_t)col < bt_ld) {
-          const int blk = block_table[(int64_t)(r - first) * bt_stride + (int64_t)req * bt_ld + col];
-          slot = blk * bs + l % bs;
-          sh = r - first;
-        }
+  // local position -> block-table column for the ids this shard keeps
+  int col[E], off[E];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    col[e] = -1;
+    off[e] = 0;
+    if (req_ok && g[e] >= 0 && owner_of(g[e], S, I) == r) {
+      const int l = local_of(g[e], S, I);
+      const int c = l / bs;
+      if ((int64_t)c < bt_ld) {
+        col[e] = c;
+        off[e] = l - c * bs;
+        ++cnt;
       }
     }
-    uint32_t my_rank = 0;
-    for (int s = 0; s < count; ++s) {
-      const uint64_t m = __ballot(sh == s);
-      if (lane == 0) s_wave[s][wave] = (uint32_t)__popcll(m);
-      if (sh == s) my_rank = (uint32_t)__popcll(m & lt_mask);
-    }
-    __syncthreads();
-    if (sh >= 0) {
-      uint32_t pos = s_run[sh] + my_rank;
-      for (int w = 0; w < wave; ++w) pos += s_wave[sh][w];
-      if (pos < (uint32_t)k) slots[((int64_t)sh * rows + row) * k + pos] = slot;
-    }
-    __syncthreads();
-    if (tid < count) {
-      uint32_t add = 0;
-      for (int w = 0; w < NW; ++w) add += s_wave[tid][w];
-      s_run[tid] += add;
-    }
-    __syncthreads();
   }
+  int blk[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) blk[e] = col[e] >= 0 ? bt[col[e]] : 0;
 
-  for (int s = 0; s < count; ++s) {
-    const uint32_t c = s_run[s];
-    int* dst = slots + ((int64_t)s * rows + row) * k;
-    for (int i = (int)c + tid; i < k; i += NT) dst[i] = -1;
-    if (tid == 0 && counts) counts[(int64_t)s * rows + row] = (int)c;
+  uint32_t total;
+  uint32_t pos = block_scan_excl<NT>(cnt, s_scan, total);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (col[e] >= 0) dst[pos++] = blk[e] * bs + off[e];
   }
+  for (int i = (int)total + tid; i < k; i += NT) dst[i] = -1;
+  if (tid == 0 && counts) counts[(int64_t)j * rows + row] = (int)total;
 }
 
 int launch_convert_index(const int* ids, int rows, int k, const int* row_req, int num_reqs,
                          const int* block_table, int64_t bt_ld, int64_t bt_stride, int bs,
                          int S, int I, int first, int count, int* slots, int* counts,
                          hipStream_t stream) {
-  hipLaunchKernelGGL(convert_index_kernel, dim3(rows), dim3(kConvThreads), 0, stream, ids,
-                     rows, k, row_req, num_reqs, block_table, bt_ld, bt_stride, bs, S, I,
-                     first, count, slots, counts);
+  const int vec = ((uintptr_t)ids % 8 == 0) ? 1 : 0;
+  dim3 grid(rows, count);
+#define DSA_CONVERT(E)                                                                          \
+  hipLaunchKernelGGL((convert_index_kernel<E>), grid, dim3(kConvThreads), 0, stream, ids, rows, \
+                     k, row_req, num_reqs, block_table, bt_ld, bt_stride, bs, S, I, first,      \
+                     slots, counts, vec)
+  switch (k / kConvThreads) {   // k is 512, 1024 or 2048
+    case 2: DSA_CONVERT(2); break;
+    case 4: DSA_CONVERT(4); break;
+    default: DSA_CONVERT(8); break;
+  }
+#undef DSA_CONVERT
   return 0;
 }
 

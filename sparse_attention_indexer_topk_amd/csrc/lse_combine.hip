@@ -7,7 +7,8 @@
 // A (row, head) whose partials are all empty gets out = 0, lse = -inf.
 //
 // How: a pure streaming kernel — one thread per (row, head, 8 features),
-// 16-byte loads of every partial, fp32 accumulation, 16-byte bf16 store.
+// 16-byte loads of the partials four at a time, fp32 accumulation in
+// partial order, 16-byte bf16 store.
 #include "launchers.h"
 
 namespace dsa {
@@ -29,16 +30,30 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
   if (M != -INFINITY) {
-    for (int p = 0; p < P; ++p) {
-      const float l = plse[(int64_t)p * rh_total + rh];
-      const float w = exp2f((l - M) * kLog2eC);  // exp(-inf) = 0
-      z += w;
-      if (w == 0.f) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
-      const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+    // partials in batches of four: all four loads are in flight together
+    constexpr int B = 4;
+    for (int p0 = 0; p0 < P; p0 += B) {
+      uint4 v[B];
+      float w[B];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc[e] += w * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+      for (int b = 0; b < B; ++b) {
+        const int p = p0 + b;
+        w[b] = 0.f;
+        v[b] = make_uint4(0u, 0u, 0u, 0u);
+        if (p < P) {
+          w[b] = exp2f((plse[(int64_t)p * rh_total + rh] - M) * kLog2eC);  // exp(-inf) = 0
+          v[b] = *reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        z += w[b];
+        if (w[b] == 0.f) continue;   // an empty partial contributes nothing, whatever it holds
+        const uint32_t ws[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] += w[b] * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+      }
     }
   }
   const float inv = z > 0.f ? 1.0f / z : 0.f;

@@ -5,203 +5,290 @@
 // candidates, the k best under (larger score, then smaller global id); the
 // output lists their ids in ascending order followed by -1.
 //
-// How (one workgroup per row):
-//  1. stage the candidates' order keys in LDS (invalid ones get a key no
-//     score can have) and count the valid ones while building the first
-//     11-bit histogram;
-//  2. radix-select the threshold score key exactly as the top-K kernel does;
-//  3. if more candidates share the threshold key than are needed, radix
-//     select among them on the id (ascending, 3 x 8 bits), which makes the
-//     (score, id) order total without a 64-bit sort;
-//  4. collect the selected ids and emit them in ascending order through an
-//     LDS bitmap over the id space (16 KB per 2^17 ids; larger id ranges are
-//     swept chunk by chunk), a popcount scan giving each id its slot.
+// How (one workgroup of 1024 threads per row):
+//  1. every thread holds E candidates (interleaved 16-byte loads of
+//     candidate pairs) as (order key, id) in registers; E = 8 or 16 holds rows
+//     of up to 8K / 16K candidates, longer rows are swept in chunks that every
+//     pass re-reads from L2;
+//  2. the k-th best score key kt comes from the same two steps as in the
+//     top-K kernel: a histogram on bins linear in the score, then an exact
+//     rank of the few keys in the threshold bin (radix select on the keys
+//     when that bin is crowded);
+//  3. when fewer kt-scored candidates are taken than exist, the smallest ids
+//     among them win: their ids are ranked the same way (radix select on the
+//     ids, 3 x 8 bits, when there are many), which makes (score, id) a total
+//     order without a sort;
+//  4. the selected ids set bits of an LDS bitmap over the id range (32 KB per
+//     2^18 ids; larger ranges are swept piecewise); each thread owns a run of
+//     bitmap words and a popcount scan gives each set bit its output slot;
+//     the ids are staged in LDS and leave in one coalesced write, -1 after.
 #include "launchers.h"
 #include "select_common.h"
 
 namespace dsa {
 
-constexpr int kMergeThreads = 512;
-constexpr int kMergeCap = 16384;        // candidate keys staged in LDS (64 KB)
-constexpr int kIdChunk = 1 << 17;       // ids covered by one bitmap sweep
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeMaxK = 2048;
+constexpr int kMergeListCap = 128;
+constexpr int kIdChunk = 1 << 18;   // ids covered by one bitmap sweep
+constexpr int kIdWords = kIdChunk / 32;
+constexpr int kIdWordsPerThread = kIdWords / kMergeThreads;
 constexpr uint32_t kInvalidKey = 0xffffffffu;  // above every real key (max 0xff800000)
-constexpr int kMaxK = 2048;
 
-template <bool STAGED>
-__global__ __launch_bounds__(kMergeThreads) void merge_candidates_kernel(
-    const float2* __restrict__ cand, int n_cand, int k, int id_bound, int* __restrict__ ids) {
+struct MergeSmem {
+  uint32_t hist[2][kBins];
+  uint32_t bitmap[kIdWords];
+  int stage[kMergeMaxK];
+  uint32_t list[kMergeListCap];
+  float red[2 * (kMergeThreads / kWave)];
+  uint32_t scan[kMergeThreads / kWave];
+  uint32_t res[4];
+  uint32_t cnt;
+  uint32_t nvalid;
+};
+
+// order key -> fp32 bits; exact except that -0 comes back as +0 and every
+// NaN as one NaN, neither of which changes a bin or a comparison
+__device__ __forceinline__ uint32_t key_to_bits(uint32_t key) {
+  return (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
+}
+
+template <int E, bool RESIDENT>
+__device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict__ src,
+                                          int n_cand, int k, int id_bound, bool vec,
+                                          int* __restrict__ out) {
   constexpr int NT = kMergeThreads;
-  __shared__ uint32_t s_keys[STAGED ? kMergeCap : 1];
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_bitmap[kIdChunk / 32];
-  __shared__ int s_list[kMaxK];
-  __shared__ uint32_t s_scan[NT / kWave + 1];
-  __shared__ uint32_t s_res[4];
-  __shared__ uint32_t s_nvalid;
-  __shared__ uint32_t s_nlist;
-
-  const int row = blockIdx.x;
+  constexpr int kChunk = NT * E;
   const int tid = threadIdx.x;
-  const float2* src = cand + (int64_t)row * n_cand;
-  int* out = ids + (int64_t)row * k;
+  const int nchunks = RESIDENT ? 1 : (n_cand + kChunk - 1) / kChunk;
 
-  auto cand_key = [&](const float2 c) -> uint32_t {
-    const float id = c.y;
-    const bool valid = id >= 0.0f && id < (float)id_bound;  // false for NaN
-    return valid ? order_key(__float_as_uint(c.x)) : kInvalidKey;
+  uint32_t key[E];
+  int id[E];
+  // slot e of chunk c0 is candidate c0 + 2 * (tid + NT * (e / 2)) + e % 2
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int v = 0; v < E / 2; ++v) {
+      const int i = c0 + 2 * (tid + NT * v);
+      float4 x = make_float4(0.f, -1.f, 0.f, -1.f);
+      if (vec) {
+        if (i < n_cand) x = *reinterpret_cast<const float4*>(src + 2 * (int64_t)i);  // n_cand even
+      } else {
+        if (i < n_cand) {
+          const float2 a = *reinterpret_cast<const float2*>(src + 2 * (int64_t)i);
+          x.x = a.x;
+          x.y = a.y;
+        }
+        if (i + 1 < n_cand) {
+          const float2 b = *reinterpret_cast<const float2*>(src + 2 * (int64_t)(i + 1));
+          x.z = b.x;
+          x.w = b.y;
+        }
+      }
+      const bool ok0 = x.y >= 0.0f && x.y < (float)id_bound;   // false for NaN
+      const bool ok1 = x.w >= 0.0f && x.w < (float)id_bound;
+      key[2 * v] = ok0 ? order_key(__float_as_uint(x.x)) : kInvalidKey;
+      key[2 * v + 1] = ok1 ? order_key(__float_as_uint(x.z)) : kInvalidKey;
+      id[2 * v] = ok0 ? (int)x.y : -1;
+      id[2 * v + 1] = ok1 ? (int)x.w : -1;
+    }
   };
-  auto key_at = [&](int i) -> uint32_t {
-    if constexpr (STAGED) return s_keys[i];
-    else return cand_key(src[i]);
+  auto sweep = [&](auto f) {
+    for (int c = 0; c < nchunks; ++c) {
+      if (!RESIDENT) load(c * kChunk);
+      f();
+    }
   };
-  auto id_at = [&](int i) -> int { return (int)src[i].y; };
 
-  // ---- 1. stage keys, count valid, first histogram ------------------------
-  clear_hist<NT>(s_hist, kBins);
-  if (tid == 0) { s_nvalid = 0; s_nlist = 0; }
-  __syncthreads();
+  // ---- 1. valid count, min / max of the finite valid scores ---------------
+  if (RESIDENT) load(0);
+  float vmin = INFINITY, vmax = -INFINITY;
   uint32_t my_valid = 0;
-  for (int i = tid; i < n_cand; i += NT) {
-    const uint32_t key = cand_key(src[i]);
-    if constexpr (STAGED) s_keys[i] = key;
-    if (key != kInvalidKey) {
-      ++my_valid;
-      atomicAdd(&s_hist[key >> 21], 1u);
+  sweep([&]() {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = key[e] != kInvalidKey;
+      const uint32_t bits = key_to_bits(key[e]);
+      const bool fin = ok && finite_bits(bits);
+      my_valid += ok ? 1u : 0u;
+      vmin = fminf(vmin, fin ? __uint_as_float(bits) : INFINITY);
+      vmax = fmaxf(vmax, fin ? __uint_as_float(bits) : -INFINITY);
     }
+  });
+  clear_words<NT>(sm.hist[0], kBins);
+  if (tid == 0) {
+    sm.cnt = 0;
+    sm.nvalid = 0;
   }
-  if (my_valid) atomicAdd(&s_nvalid, my_valid);
   __syncthreads();
-  const uint32_t n_valid = s_nvalid;
+  {
+    const uint32_t w = wave_scan_incl(my_valid);
+    if (lane_id() == kWave - 1 && w) atomicAdd(&sm.nvalid, w);
+  }
+  block_min_max<NT>(vmin, vmax, sm.red);
+  const uint32_t n_valid = sm.nvalid;
+  const LinBins lb = make_lin_bins(vmin, vmax);
 
-  // ---- 2/3. threshold (score key, then id among equal keys) ---------------
-  uint32_t prefix = 0;
-  int shift = 32;        // shift == 32: every valid candidate is selected
-  bool tie_by_id = false;
-  uint32_t id_thr = 0;   // with tie_by_id: take equal keys with id <= id_thr
+  // ---- 2/3. threshold: score key, then id among equal keys ---------------
+  bool take_all = true;   // every valid candidate is selected
+  uint32_t kt = 0;        // otherwise: keys above kt, ...
+  bool tie_by_id = false; // ... and kt-keyed ones, all or those with id <= id_thr
+  uint32_t id_thr = 0;
   if (n_valid > (uint32_t)k) {
-    Bucket bk = find_bucket<NT, true>(s_hist, kBins, (uint32_t)k, s_scan, s_res);
-    prefix = bk.bin;
-    shift = 21;
-    if (bk.count != bk.need) {
-      clear_hist<NT>(s_hist, kBins);
-      __syncthreads();
-      for (int i = tid; i < n_cand; i += NT) {
-        const uint32_t key = key_at(i);
-        if (key != kInvalidKey && (key >> 21) == prefix)
-          atomicAdd(&s_hist[(key >> 10) & 0x7ffu], 1u);
-      }
-      __syncthreads();
-      bk = find_bucket<NT, true>(s_hist, kBins, bk.need, s_scan, s_res);
-      prefix = (prefix << 11) | bk.bin;
-      shift = 10;
-      if (bk.count != bk.need) {
-        clear_hist<NT>(s_hist, 1024);
-        __syncthreads();
-        for (int i = tid; i < n_cand; i += NT) {
-          const uint32_t key = key_at(i);
-          if (key != kInvalidKey && (key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3ffu], 1u);
-        }
-        __syncthreads();
-        bk = find_bucket<NT, true>(s_hist, 1024, bk.need, s_scan, s_res);
-        prefix = (prefix << 10) | bk.bin;
-        shift = 0;
-        if (bk.count != bk.need) {
-          // equal full keys: take the `need` smallest ids (ids < 2^24)
-          tie_by_id = true;
-          uint32_t need = bk.need;
-          uint32_t id_prefix = 0;
-          for (int level = 0; level < 3; ++level) {
-            const int ishift = 16 - 8 * level;
-            clear_hist<NT>(s_hist, 256);
-            __syncthreads();
-            for (int i = tid; i < n_cand; i += NT) {
-              if (key_at(i) != prefix) continue;
-              const uint32_t id = (uint32_t)id_at(i);
-              if (level == 0 || (id >> (ishift + 8)) == id_prefix)
-                atomicAdd(&s_hist[(id >> ishift) & 0xffu], 1u);
-            }
-            __syncthreads();
-            Bucket ib = find_bucket<NT, false>(s_hist, 256, need, s_scan, s_res);
-            id_prefix = (id_prefix << 8) | ib.bin;
-            need = ib.need;
+    take_all = false;
+    sweep([&]() {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        atomicAdd(&sm.hist[0][lin_bin(key_to_bits(key[e]), lb)], key[e] != kInvalidKey ? 1u : 0u);
+    });
+    __syncthreads();
+    const Bucket bk = block_find_bucket<true>(sm.hist[0], kBins, (uint32_t)k, sm.res);
+    uint32_t take, n_kt;
+    if (bk.count <= (uint32_t)kMergeListCap) {
+      sweep([&]() {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (key[e] != kInvalidKey && lin_bin(key_to_bits(key[e]), lb) == bk.bin) {
+            const uint32_t slot = atomicAdd(&sm.cnt, 1u);
+            sm.list[slot] = key[e];   // slot < count <= the list capacity
           }
-          id_thr = id_prefix;  // exactly one candidate has this id
         }
-      }
-    }
-  }
-
-  // ---- 4a. collect the selected ids ----------------------------------------
-  for (int i = tid; i < n_cand; i += NT) {
-    const uint32_t key = key_at(i);
-    if (key == kInvalidKey) continue;
-    bool sel;
-    if (shift == 32) {
-      sel = true;
+      });
+      __syncthreads();
+      list_threshold<NT>(sm.list, (int)bk.count, bk.need, sm.res);
+      kt = sm.res[0];
+      take = sm.res[1];
+      n_kt = sm.res[2];
+      __syncthreads();   // res and the list are reused below
     } else {
-      const uint32_t p = key >> shift;
-      sel = p > prefix;
-      if (p == prefix) sel = !tie_by_id || (uint32_t)id_at(i) <= id_thr;
+      radix_threshold<NT>(sm.hist, sm.res, (uint32_t)k, [&](auto f) {
+        sweep([&]() {
+#pragma unroll
+          for (int e = 0; e < E; ++e) f(key[e], key[e] != kInvalidKey);
+        });
+      }, &kt, &take, &n_kt);
     }
-    if (sel) {
-      const uint32_t slot = atomicAdd(&s_nlist, 1u);
-      if (slot < (uint32_t)kMaxK) s_list[slot] = id_at(i);
-    }
-  }
-  __syncthreads();
-  uint32_t n_list = s_nlist;
-  if (n_list > (uint32_t)k) n_list = (uint32_t)k;
-
-  // ---- 4b. ascending-id output through the bitmap ---------------------------
-  constexpr int kWords = kIdChunk / 32;
-  constexpr int kWpt = kWords / NT;  // words per thread
-  uint32_t written = 0;
-  for (int c0 = 0; c0 < id_bound; c0 += kIdChunk) {
-    for (int w = tid; w < kWords; w += NT) s_bitmap[w] = 0u;
-    __syncthreads();
-    for (int i = tid; i < (int)n_list; i += NT) {
-      const int id = s_list[i];
-      if (id >= c0 && id < c0 + kIdChunk) {
-        const int off = id - c0;
-        atomicOr(&s_bitmap[off >> 5], 1u << (off & 31));
+    if (take < n_kt) {
+      // the `take` smallest ids among the kt-keyed candidates (distinct ids)
+      tie_by_id = true;
+      if (n_kt <= (uint32_t)kMergeListCap) {
+        if (tid == 0) sm.cnt = 0;
+        __syncthreads();
+        sweep([&]() {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (key[e] == kt) {
+              const uint32_t slot = atomicAdd(&sm.cnt, 1u);
+              sm.list[slot] = (uint32_t)id[e];
+            }
+          }
+        });
+        __syncthreads();
+        if (tid < (int)n_kt) {
+          const uint32_t mine = sm.list[tid];
+          uint32_t below = 0;
+          for (int j = 0; j < (int)n_kt; ++j) below += sm.list[j] < mine ? 1u : 0u;
+          if (below == take - 1) sm.res[3] = mine;
+        }
+        __syncthreads();
+        id_thr = sm.res[3];
+      } else {
+        uint32_t need = take, id_prefix = 0;
+        for (int level = 0; level < 3; ++level) {
+          const int ishift = 16 - 8 * level;
+          clear_words<NT>(sm.hist[0], 256);
+          __syncthreads();
+          sweep([&]() {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const uint32_t u = (uint32_t)id[e];
+              if (key[e] == kt && (level == 0 || (u >> (ishift + 8)) == id_prefix))
+                atomicAdd(&sm.hist[0][(u >> ishift) & 0xffu], 1u);
+            }
+          });
+          __syncthreads();
+          const Bucket ib = block_find_bucket<false>(sm.hist[0], 256, need, sm.res);
+          id_prefix = (id_prefix << 8) | ib.bin;
+          need = ib.need;
+          __syncthreads();   // res and the histogram are rewritten next level
+        }
+        id_thr = id_prefix;   // ids < 2^24: three digits cover them
       }
     }
+  }
+  const uint32_t n_sel = n_valid < (uint32_t)k ? n_valid : (uint32_t)k;
+
+  // ---- 4. ascending-id output through the bitmap --------------------------
+  auto selected = [&](int e) {
+    if (key[e] == kInvalidKey) return false;
+    if (take_all || key[e] > kt) return true;
+    return key[e] == kt && (!tie_by_id || (uint32_t)id[e] <= id_thr);
+  };
+  uint32_t written = 0;
+  for (int b0 = 0; b0 < id_bound && written < n_sel; b0 += kIdChunk) {
+    const int span = (id_bound - b0) < kIdChunk ? (id_bound - b0) : kIdChunk;
+    const int nwords = (span + 31) >> 5;
+    const int wpt = (nwords + NT - 1) / NT;   // words per thread, <= kIdWordsPerThread
+    for (int w = tid; w < nwords; w += NT) sm.bitmap[w] = 0u;
     __syncthreads();
-    uint32_t words[kWpt];
+    sweep([&]() {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int off = id[e] - b0;
+        if (off >= 0 && off < span && selected(e))
+          atomicOr(&sm.bitmap[off >> 5], 1u << (off & 31));
+      }
+    });
+    __syncthreads();
+    uint32_t words[kIdWordsPerThread];
     uint32_t cnt = 0;
 #pragma unroll
-    for (int q = 0; q < kWpt; ++q) {
-      words[q] = s_bitmap[tid * kWpt + q];
+    for (int q = 0; q < kIdWordsPerThread; ++q) {
+      const int w = tid * wpt + q;
+      words[q] = (q < wpt && w < nwords) ? sm.bitmap[w] : 0u;
       cnt += __popc(words[q]);
     }
     uint32_t total;
-    uint32_t pos = written + block_excl_scan<NT>(cnt, s_scan, total);
+    uint32_t pos = written + block_scan_excl<NT>(cnt, sm.scan, total);
 #pragma unroll
-    for (int q = 0; q < kWpt; ++q) {
+    for (int q = 0; q < kIdWordsPerThread; ++q) {
       uint32_t w = words[q];
       while (w) {
-        const int b = __ffs(w) - 1;
+        const int b = __builtin_ctz(w);
         w &= w - 1;
-        if (pos < (uint32_t)k) out[pos] = c0 + (tid * kWpt + q) * 32 + b;
+        if (pos < (uint32_t)k) sm.stage[pos] = b0 + (tid * wpt + q) * 32 + b;
         ++pos;
       }
     }
     written += total;
-    if (written >= n_list) break;  // uniform: total is block-wide
   }
-  for (int i = (int)n_list + tid; i < k; i += NT) out[i] = -1;
+  __syncthreads();
+  const int n_out = (int)(written < (uint32_t)k ? written : (uint32_t)k);
+  for (int i = tid; i < k; i += NT) out[i] = i < n_out ? sm.stage[i] : -1;
+}
+
+template <int E>
+__global__ __launch_bounds__(kMergeThreads) void merge_candidates_kernel(
+    const float* __restrict__ cand, int n_cand, int k, int id_bound, int* __restrict__ ids,
+    int vec) {
+  __shared__ MergeSmem sm;
+  const int row = blockIdx.x;
+  const float* src = cand + (int64_t)row * n_cand * 2;
+  int* out = ids + (int64_t)row * k;
+  if (n_cand <= kMergeThreads * E)
+    merge_row<E, true>(sm, src, n_cand, k, id_bound, vec != 0, out);
+  else
+    merge_row<E, false>(sm, src, n_cand, k, id_bound, vec != 0, out);
 }
 
 int launch_merge_candidates(const float* cand, int rows, int n_cand, int k, int id_bound,
                             int* ids, hipStream_t stream) {
-  const float2* c2 = reinterpret_cast<const float2*>(cand);
-  if (n_cand <= kMergeCap) {
-    hipLaunchKernelGGL(merge_candidates_kernel<true>, dim3(rows), dim3(kMergeThreads), 0,
-                       stream, c2, n_cand, k, id_bound, ids);
-  } else {
-    hipLaunchKernelGGL(merge_candidates_kernel<false>, dim3(rows), dim3(kMergeThreads), 0,
-                       stream, c2, n_cand, k, id_bound, ids);
-  }
+  const int vec = ((uintptr_t)cand % 16 == 0 && n_cand % 2 == 0) ? 1 : 0;
+  if (n_cand <= kMergeThreads * 8)
+    hipLaunchKernelGGL((merge_candidates_kernel<8>), dim3(rows), dim3(kMergeThreads), 0, stream,
+                       cand, n_cand, k, id_bound, ids, vec);
+  else
+    hipLaunchKernelGGL((merge_candidates_kernel<16>), dim3(rows), dim3(kMergeThreads), 0,
+                       stream, cand, n_cand, k, id_bound, ids, vec);
   return 0;
 }
 

@@ -1,4 +1,4 @@
-// Radix-select building blocks shared by the top-K and merge kernels.
+// Radix-select building blocks shared by the top-K, merge and convert kernels.
 #pragma once
 
 #include "dsa_common.h"
@@ -13,45 +13,231 @@ struct Bucket {
   uint32_t count;  // how many elements it holds
 };
 
-// Walks a histogram of `nbins` bins from the top bin down (DESC) or from bin
-// 0 up (!DESC) and finds the bin in which the running count reaches `need`.
-// Every thread of the block must call it; on return every thread sees the
-// same result.  `scan` holds >= NT/64 + 1 words, `res` 3 words of LDS.
-template <int NT, bool DESC>
-__device__ Bucket find_bucket(const uint32_t* hist, int nbins, uint32_t need,
-                              uint32_t* scan, uint32_t* res) {
-  constexpr int kPer = kBins / NT;  // bins per thread (nbins <= kBins)
-  const int t = threadIdx.x;
-  uint32_t c[kPer];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int d = t * kPer + q;  // rank of the bin in walking order
-    const int bin = DESC ? nbins - 1 - d : d;
-    c[q] = d < nbins ? hist[bin] : 0u;
-    sum += c[q];
-  }
-  uint32_t total;
-  uint32_t before = block_excl_scan<NT>(sum, scan, total);
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int d = t * kPer + q;
-    if (d < nbins && before < need && before + c[q] >= need) {
-      res[0] = (uint32_t)(DESC ? nbins - 1 - d : d);
-      res[1] = need - before;
-      res[2] = c[q];
-    }
-    before += c[q];
-  }
+// ---------------------------------------------------------------- DPP ------
+// DPP controls of the gfx9 family (wave64): row_shr:n shifts within a 16-lane
+// row, row_bcast:15 / row_bcast:31 carry a row's last lane into the next rows.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave (uint32, wrapping), built
+// from DPP row shifts and row broadcasts — no LDS round trips.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr1, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr2, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr4, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr8, 0xf, 0xf, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast15, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowBcast31, 0xc, 0xf, false);
+  return v;
+}
+
+// Block-wide exclusive prefix sum: a DPP wave scan, the wave totals through
+// LDS (`scratch`, >= NT/64 words) and one barrier.  Returns the thread's
+// exclusive prefix and the block total.  Every thread must call it; the
+// caller must not rewrite `scratch` before a later barrier.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* scratch,
+                                                    uint32_t& total) {
+  constexpr int NW = NT / kWave;
+  const int wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_scan_incl(v);
+  if (lane_id() == kWave - 1) scratch[wave] = incl;
   __syncthreads();
-  Bucket b{res[0], res[1], res[2]};
-  __syncthreads();  // res may be rewritten by the next call
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = scratch[w];
+    before += (w < wave) ? s : 0u;
+    all += s;
+  }
+  total = all;
+  return before + incl - v;
+}
+
+// Finds, in a histogram of `nbins` (a multiple of 64, at most 2048) bins, the
+// bin where the running count, walked from the top bin down (DESC) or from
+// bin 0 up (!DESC), reaches `need`.  Runs in ONE wave: each lane sums a
+// contiguous run of bins, a DPP scan locates the owning lane, then the lanes
+// scan that run.  The caller publishes the result through LDS.
+template <bool DESC>
+__device__ __forceinline__ Bucket wave_find_bucket(const uint32_t* hist, int nbins,
+                                                   uint32_t need) {
+  const int lane = lane_id();
+  const int per = nbins / kWave;                       // bins per lane (<= 32)
+  auto bin_of = [&](int rank) { return DESC ? nbins - 1 - rank : rank; };
+  uint32_t sum = 0;
+  for (int j = 0; j < per; ++j) {
+    const int r = lane * per + ((j + lane) & (per - 1));   // rotated: fewer bank conflicts
+    sum += hist[bin_of(r)];
+  }
+  const uint32_t incl = wave_scan_incl(sum);
+  const uint32_t before = incl - sum;
+  const uint64_t hit = __ballot(before < need && incl >= need);
+  // need <= the histogram's total, so some lane holds it; the guard keeps a
+  // corrupted count from indexing past the histogram
+  const int owner = hit ? (int)__builtin_ctzll(hit) : kWave - 1;
+  const uint32_t ob = (uint32_t)__builtin_amdgcn_readlane((int)before, owner);
+  const uint32_t c = lane < per ? hist[bin_of(owner * per + lane)] : 0u;
+  const uint32_t ci = wave_scan_incl(c);
+  const uint64_t hit2 = __ballot(lane < per && ob + ci - c < need && ob + ci >= need);
+  const int j = hit2 ? (int)__builtin_ctzll(hit2) : per - 1;
+  const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+  const uint32_t cij = (uint32_t)__builtin_amdgcn_readlane((int)ci, j);
+  Bucket b;
+  b.bin = (uint32_t)bin_of(owner * per + j);
+  b.need = need - (ob + cij - cj);
+  b.count = cj;
   return b;
 }
 
+// Wave 0 finds the bucket and publishes it in `res` (3 words of LDS); after
+// the barrier every thread reads it.  The histogram must be complete (a
+// barrier between its last update and this call).
+template <bool DESC>
+__device__ __forceinline__ Bucket block_find_bucket(const uint32_t* hist, int nbins, uint32_t need,
+                                                    uint32_t* res) {
+  if (threadIdx.x < kWave) {
+    const Bucket b = wave_find_bucket<DESC>(hist, nbins, need);
+    if (threadIdx.x == 0) {
+      res[0] = b.bin;
+      res[1] = b.need;
+      res[2] = b.count;
+    }
+  }
+  __syncthreads();
+  return Bucket{res[0], res[1], res[2]};
+}
+
 template <int NT>
-__device__ __forceinline__ void clear_hist(uint32_t* hist, int n) {
-  for (int i = threadIdx.x; i < n; i += NT) hist[i] = 0u;
+__device__ __forceinline__ void clear_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += NT) p[i] = 0u;
+}
+
+// ------------------------------------------------ linear score bins -------
+// First-pass bins that are linear in the score between the row's smallest and
+// largest finite valid score: unlike the top bits of the order key (which
+// group by binary exponent, so that typical logits crowd into a dozen bins)
+// they spread the scores evenly, and the bin holding the k-th best score
+// usually holds only a handful of elements.  The map is monotone in the
+// score order of order_key (NaN and -inf in bin 0, +inf in the last bin;
+// finite scores through a rounded subtract and multiply, both monotone), so
+// "bin above b" implies "key above every key of bin b".
+struct LinBins {
+  float lo_half;  // smallest finite score / 2
+  float scale;    // bins per unit of (score / 2); 0 when every score shares one bin
+};
+
+__device__ __forceinline__ LinBins make_lin_bins(float vmin, float vmax) {
+  LinBins lb{0.f, 0.f};
+  if (vmin <= vmax) {   // at least one finite score
+    lb.lo_half = vmin * 0.5f;
+    const float range = vmax * 0.5f - lb.lo_half;  // halves: no overflow
+    const float sc = range > 0.f ? (float)kBins / range : 0.f;
+    lb.scale = sc <= 3.0e38f ? sc : 0.f;           // a range too small to divide
+  }
+  return lb;
+}
+
+__device__ __forceinline__ uint32_t lin_bin(uint32_t bits, LinBins lb) {
+  if ((bits & 0x7f800000u) == 0x7f800000u) return bits == 0x7f800000u ? kBins - 1 : 0u;
+  // t >= 0 for every score >= the minimum; the clamps keep any other value
+  // (a slot outside the valid range, counted with weight 0) inside the table
+  const float t = (__uint_as_float(bits) * 0.5f - lb.lo_half) * lb.scale;
+  return (uint32_t)fminf(fmaxf(t, 0.f), (float)(kBins - 1));
+}
+
+__device__ __forceinline__ bool finite_bits(uint32_t bits) {
+  return (bits & 0x7f800000u) != 0x7f800000u;
+}
+
+// Min and max over the block; `scratch` holds 2 * NT/64 floats.  One barrier.
+template <int NT>
+__device__ __forceinline__ void block_min_max(float& vmin, float& vmax, float* scratch) {
+  constexpr int NW = NT / kWave;
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) {
+    vmin = fminf(vmin, __shfl_xor(vmin, d, kWave));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, d, kWave));
+  }
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    scratch[wave] = vmin;
+    scratch[NW + wave] = vmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    vmin = fminf(vmin, scratch[w]);
+    vmax = fmaxf(vmax, scratch[NW + w]);
+  }
+}
+
+// Exact threshold among the `c` order keys in `list` (c <= NT): the
+// `need`-th largest key kt, and how many elements equal to kt are taken
+// (need minus the keys above kt).  The thread holding a key with
+// (#keys above) < need <= (#keys at or above) publishes the pair; all such
+// threads hold kt and write the same words.  One barrier; the result is in
+// res[0] (kt), res[1] (take) and res[2] (how many keys equal kt).
+template <int NT>
+__device__ __forceinline__ void list_threshold(const uint32_t* list, int c, uint32_t need,
+                                               uint32_t* res) {
+  const int tid = threadIdx.x;
+  if (tid < c) {
+    const uint32_t kx = list[tid];
+    uint32_t above = 0, at_least = 0;
+    for (int j = 0; j < c; ++j) {
+      const uint32_t kj = list[j];
+      above += kj > kx ? 1u : 0u;
+      at_least += kj >= kx ? 1u : 0u;
+    }
+    if (above < need && need <= at_least) {
+      res[0] = kx;
+      res[1] = need - above;
+      res[2] = at_least - above;   // how many keys equal kt
+    }
+  }
+  __syncthreads();
+}
+
+// Radix select of the `need`-th largest key over all valid elements, 11/11/10
+// bits (the fallback when a linear bin is crowded, e.g. all scores equal).
+// `for_keys(f)` calls f(key, valid) for every element of the block's row.
+// Returns kt, how many kt-equal elements to take, and how many there are.
+// Uses both histograms; ends with a barrier, so `res` and the histograms may
+// be reused afterwards.
+template <int NT, typename ForKeys>
+__device__ __forceinline__ void radix_threshold(uint32_t (*hist)[kBins], uint32_t* res,
+                                                uint32_t need, ForKeys for_keys, uint32_t* kt,
+                                                uint32_t* take, uint32_t* n_kt) {
+  clear_words<NT>(hist[0], kBins);
+  clear_words<NT>(hist[1], kBins);
+  __syncthreads();
+  for_keys([&](uint32_t key, bool ok) {
+    if (ok) atomicAdd(&hist[0][key >> 21], 1u);
+  });
+  __syncthreads();
+  Bucket bk = block_find_bucket<true>(hist[0], kBins, need, res);
+  uint32_t prefix = bk.bin;
+  for_keys([&](uint32_t key, bool ok) {
+    if (ok && (key >> 21) == prefix) atomicAdd(&hist[1][(key >> 10) & 0x7ffu], 1u);
+  });
+  clear_words<NT>(hist[0], 1024);
+  __syncthreads();
+  bk = block_find_bucket<true>(hist[1], kBins, bk.need, res);
+  prefix = (prefix << 11) | bk.bin;
+  for_keys([&](uint32_t key, bool ok) {
+    if (ok && (key >> 10) == prefix) atomicAdd(&hist[0][key & 0x3ffu], 1u);
+  });
+  __syncthreads();
+  bk = block_find_bucket<true>(hist[0], 1024, bk.need, res);
+  *kt = (prefix << 10) | bk.bin;
+  *take = bk.need;
+  *n_kt = bk.count;
+  __syncthreads();
 }
 
 }  // namespace dsa

@@ -19,10 +19,13 @@
 //    all 128 heads;
 //  - the part's slot list is staged once in LDS; the selected latent rows are
 //    gathered 32 tokens per tile straight from HBM into LDS with
-//    global_load_lds_dwordx4 (no register staging) through a 3-stage ring, so
-//    two tiles are in flight while one is consumed; 16-byte chunks of a row
-//    are XOR-swizzled by (token & 7) so the 32 rows one MFMA operand read
-//    touches fall in distinct LDS banks;
+//    global_load_lds_dwordx4 (no register staging) through a 3-stage ring:
+//    tile t+1 is in flight while tile t is consumed, and a stage is reused
+//    only after the barrier that follows its last reader; two barriers per
+//    tile (tile arrival, score exchange);
+//  - the 16-byte chunks of a row are XOR-swizzled (swz_key) so that both the
+//    score-operand reads and the value transpose reads are free of bank
+//    conflicts;
 //  - scores are computed transposed, S^T = K Q^T (rows = tokens), so the
 //    accumulator gives each lane 16 tokens of ONE head — exactly the B
 //    operand (P^T) of the value product O^T += V^T P^T;
@@ -86,7 +89,10 @@ __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 // byte offset of logical 16-byte chunk c of token row t inside a bf16 tile
-__device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ (t & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int t) {
+  return ((t >> 1) & 1) | (((t ^ (t >> 2)) & 1) << 1) | (((t ^ (t >> 1) ^ (t >> 3)) & 1) << 2);
+}
+__device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ swz_key(t)) << 4); }
 
 template <bool FP8>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
@@ -168,22 +174,39 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   for (int i = 0; i < 4; ++i) qk_off[i] = chunk_off(j32, 36 * u + g + 2 * i);
   // values (transpose reads): 16-lane group G = lane/16 has k-group g = G/2
   // and feature half fs = G%2; inside it, source role sp = lane%16 reads
-  // token row 8*(2*ks + h) + 4*g + sp/4 at features
-  // 256u + 32mb + 16fs + 4(sp%4) -> pv_off[mb % 2] + 8*(2ks+h)*row + 128*(mb/2)
-  int pv_off[2];
+  // token row 16*ks + 8*h + 4*g + sp/4 at features 256u + 32mb + 16fs +
+  // 4(sp%4) -> pv_off[mb % 2][h] + 16*ks*row + 128*(mb/2) (the swizzle key is
+  // linear and ignores row bit 4, so only h changes the per-lane base)
+  int pv_off[2][2];
   {
     const int sp = lane & 15, fs = (lane >> 4) & 1;
     const int trb = 4 * g + (sp >> 2);
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int feat = 256 * u + 32 * par + 16 * fs + 4 * (sp & 3);
-      pv_off[par] = chunk_off(trb, feat >> 3) + (feat & 7) * 2;
-    }
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int feat = 256 * u + 32 * par + 16 * fs + 4 * (sp & 3);
+        pv_off[par][h] = chunk_off(trb + 8 * h, feat >> 3) + (feat & 7) * 2;
+      }
   }
 
   // ---- DMA issue of tile tt into its ring stage -------------------------------
   // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
   // instructions are dealt round-robin to the waves.
+  int dma_to[kDmaMax];
+#pragma unroll
+  for (int jj = 0; jj < kDmaMax; ++jj) {
+    const int p = (jj * kAttnWaves + wave) * kWave + lane;
+    int t, off;
+    if constexpr (FP8) {
+      t = p / (kRowB8 / 16);
+      off = (p % (kRowB8 / 16)) * 16;
+    } else {
+      t = p / kRowChunks;
+      off = ((p % kRowChunks) ^ swz_key(t)) * 16;
+    }
+    dma_to[jj] = (t & 31) | (off << 8);
+  }
   auto issue = [&](int tt) {
     uint8_t* stage = s_ring[tt % kStages];
     const int tbase = tt * kTile;
@@ -191,19 +214,10 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
       if (ins < kDmaTotal) {
-        int p = ins * kWave + lane;
-        asm volatile("" : "+v"(p));   // recompute per issue: keep it out of loop-invariant VGPRs
-        int t, off;
-        if constexpr (FP8) {
-          t = p / (kRowB8 / 16);                       // raw rows, unswizzled
-          off = (p % (kRowB8 / 16)) * 16;
-        } else {
-          t = p / kRowChunks;                          // chunk slot -> logical chunk
-          off = ((p % kRowChunks) ^ (t & 7)) * 16;
-        }
+        const int t = dma_to[jj] & 31;
         const int ti = tbase + t < n_tok ? tbase + t : 0;
-        const int s = max(s_slot[ti], 0);              // masked later; any valid row
-        const uint8_t* src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + off;
+        const int s = max(s_slot[ti], 0);
+        const uint8_t* src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + (dma_to[jj] >> 8);
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (lds_void_ptr)(stage + ins * kWave * 16), 16, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -213,24 +227,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // this wave's DMA instructions per tile
   const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  int next_issue = 0;   // next tile whose DMA has not been issued
-  for (int tt = 0; tt < ntiles;) {
-    // keep two tiles in flight beyond tile tt (fills the ring at the start
-    // and after a restart)
-    while (next_issue < ntiles && next_issue <= tt + 2) issue(next_issue++);
-    // wait for this wave's DMA of tile tt; younger tiles may stay in flight
-    switch ((next_issue - 1 - tt) * my_dma) {
-      case 10: vm_wait<10>(); break;
-      case 9: vm_wait<9>(); break;
-      case 8: vm_wait<8>(); break;
-      case 6: vm_wait<6>(); break;
-      case 5: vm_wait<5>(); break;
-      case 4: vm_wait<4>(); break;
-      case 3: vm_wait<3>(); break;
-      case 2: vm_wait<2>(); break;
-      default: vm_wait<0>(); break;
+  // Iteration tt issues tile tt+1 into the stage tile tt-2 used (free since
+  // the previous iteration's first barrier), waits for tile tt and computes
+  // it.  A restart request raised while computing tile tt is seen at the next
+  // barrier: inside the loop at the next tile's arrival barrier, after the
+  // last tile at the barrier below the loop.
+  int next_issue = 0;
+  int tt = 0;
+  for (;;) {
+  for (; tt < ntiles;) {
+    while (next_issue < ntiles && next_issue <= tt + 1) issue(next_issue++);
+    if (next_issue - 1 > tt) {
+      if (my_dma == 5) vm_wait<5>();
+      else if (my_dma == 4) vm_wait<4>();
+      else if (my_dma == 3) vm_wait<3>();
+      else vm_wait<2>();
+    } else {
+      vm_wait<0>();
     }
-    bar();
+    lgkm_wait0();
+    bar();   // tile tt visible; every wave is done with tile tt-1
+    if (s_restart) {
+      // a reference max moved by more than 2^64: drop the partial sums and
+      // replay the token list (every wave, since the tile ring is shared)
+      vm_wait<0>();
+      bar();
+      if (tid == 0) s_restart = 0;
+#pragma unroll
+      for (int mb = 0; mb < kOBlocks; ++mb)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+      l_part = 0.f;
+      __syncthreads();
+      tt = 0;
+      next_issue = 0;
+      continue;
+    }
 
     const uint8_t* tile = s_ring[tt % kStages];
     if constexpr (FP8) {
@@ -294,27 +326,27 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         sacc[4 * a4 + 3] += x.w;
       }
       // lane holds head `head`, tokens 8*(a/4) + 4*g + a%4 (same in both members)
-      // this lane's tokens 8*b + 4*g + r: shift the tile mask by 4*g once,
-      // then test the constant bit 8*b + r
-      const uint32_t vm = (uint32_t)(vmask >> (4 * g));
-      float sv[16];
-      float mt = -INFINITY;
+      if (vmask != 0xffffffffull) {
+        const uint32_t vm = (uint32_t)(vmask >> (4 * g));
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        sv[a] = ((vm >> (8 * (a >> 2) + (a & 3))) & 1u) ? sacc[a] * qk_scale : -INFINITY;
-        mt = fmaxf(mt, sv[a]);
+        for (int a = 0; a < 16; ++a)
+          if (!((vm >> (8 * (a >> 2) + (a & 3))) & 1u)) sacc[a] = -INFINITY;
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      float mt = sacc[0];
+#pragma unroll
+      for (int a = 1; a < 16; ++a) mt = fmaxf(mt, sacc[a]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * qk_scale;
       if (m_ref == -INFINITY) {
-        m_ref = mt;                        // first tile with a valid token
+        m_ref = mt;
       } else if (__any(mt > m_ref + kRestartSlack)) {
-        m_ref = fmaxf(m_ref, mt);          // raise, then restart (below)
+        m_ref = fmaxf(m_ref, mt);
         if (lane == 0) s_restart = 1;
       }
+      const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
       bf16x8_t pf0, pf1;   // probabilities, rounded to nearest even by the hardware
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const float p = (m_ref == -INFINITY) ? 0.f : exp2f(sv[a] - m_ref);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[a], qk_scale, nm));
         l_part += p;
         if (a < 8) pf0[a] = static_cast<__bf16>(p);
         else pf1[a - 8] = static_cast<__bf16>(p);
@@ -330,7 +362,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(
-              tile + pv_off[mb & 1] + 8 * (2 * ks + h) * kRowB + 128 * (mb >> 1)));
+              tile + pv_off[mb & 1][h] + 16 * ks * kRowB + 128 * (mb >> 1)));
         return __builtin_bit_cast(bf16x8_t,
                                   __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
@@ -342,25 +374,21 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    lgkm_wait0();
-    bar();   // stage tt % 3, s_conv and s_x free again; s_restart final
-    if (s_restart) {
-      // a reference max moved by more than 2^64: drop the partial sums and
-      // replay the token list (every wave, since the tile ring is shared)
-      vm_wait<0>();
-      bar();
-      if (tid == 0) s_restart = 0;
-#pragma unroll
-      for (int mb = 0; mb < kOBlocks; ++mb)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
-      l_part = 0.f;
-      __syncthreads();
-      tt = 0;
-      next_issue = 0;
-      continue;
-    }
     ++tt;
+  }
+  lgkm_wait0();
+  bar();
+  if (!s_restart) break;
+  bar();
+  if (tid == 0) s_restart = 0;
+#pragma unroll
+  for (int mb = 0; mb < kOBlocks; ++mb)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+  l_part = 0.f;
+  __syncthreads();
+  tt = 0;
+  next_issue = 0;
   }
 
   // ---- epilogue ---------------------------------------------------------------

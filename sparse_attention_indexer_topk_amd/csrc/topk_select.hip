@@ -7,41 +7,198 @@
 // smaller position; then each selection becomes a (score, global_id) pair in
 // the shard's k columns of the gathered candidate buffer.
 //
-// How (one workgroup per (row, shard)):
-//  1. stream the row's valid logits from HBM with 16-byte loads into LDS
-//     (raw bits), building a 2048-bin histogram of the top 11 bits of the
-//     order-preserving key on the way;
-//  2. walk the histogram from the top to find the bin holding the k-th key;
-//     refine inside that bin with the next 11, then the last 10 key bits
-//     (each refinement re-reads LDS only) until the bin is either taken
-//     whole or the exact k-th key is known;
-//  3. one stable pass in position order: element e is selected when its key
-//     prefix is above the threshold prefix, or equal to it and among the
-//     first `need` such elements; a block-wide exclusive scan of packed
-//     (above, equal) counts gives every selection its output slot, so the
-//     output is in ascending position with no sort and no atomics.
-// Rows whose valid range holds <= k positions take everything (no select).
+// How (one workgroup of 1024 threads per (row, shard)):
+//  1. thread t holds E contiguous logits of the row in registers (16-byte
+//     loads) with their order keys; E = 8 or 16 holds rows of up to 8K / 16K
+//     local positions, longer rows are swept in chunks of 1024*E that every
+//     pass re-reads from L2;
+//  2. the k-th best key kt is found in two steps: a 2048-bin histogram on
+//     bins linear in the score between the row's min and max finite score
+//     (one wave finds the bin b where the count from the top reaches k), then
+//     the few keys of bin b are listed in LDS and ranked exactly; a bin too
+//     full to rank falls back to an 11/11/10-bit radix select on the keys;
+//  3. one stable pass in position order: an element is taken when its key is
+//     above kt, or equal to it and among the first `take` such elements; a
+//     block exclusive scan of packed (above, equal) counts gives each
+//     selection its output slot — ascending position, no sort, no atomics
+//     deciding order.  Selections are staged in LDS and written out
+//     coalesced.
+// Rows whose valid range holds <= k positions take everything.
 #include "launchers.h"
 #include "select_common.h"
 
 namespace dsa {
 
-constexpr int kTopkThreads = 512;
-constexpr int kTopkCap = 16384;  // logits staged in LDS (64 KB)
-constexpr int kTopkIpt = 4;      // elements per thread per compaction tile
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxK = 2048;
+constexpr int kTopkListCap = 128;   // threshold-bin keys ranked directly
 
-template <bool STAGED>
-__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
-    const float* __restrict__ logits, int64_t ld, int64_t shard_stride, int rows,
-    int ctx, const int* __restrict__ row_starts, const int* __restrict__ row_ends,
-    int k, int S, int I, int shard_first, int* __restrict__ local_idx,
-    float* __restrict__ cand, int vec4) {
+struct TopkSmem {
+  uint32_t hist[2][kBins];
+  uint32_t list[kTopkListCap];
+  float2 out[kTopkMaxK];
+  int idx[kTopkMaxK];
+  float red[2 * (kTopkThreads / kWave)];
+  uint32_t scan[2][kTopkThreads / kWave];
+  uint32_t res[4];
+  uint32_t cnt;
+};
+
+template <int E, bool RESIDENT>
+__device__ __forceinline__ void topk_row(TopkSmem& sm, const float* __restrict__ src, int lo,
+                                         int hi, bool vec, int k, int S, int I, int r,
+                                         int* __restrict__ oidx, float2* __restrict__ ocand,
+                                         bool out_vec) {
   constexpr int NT = kTopkThreads;
-  __shared__ __attribute__((aligned(16))) uint32_t s_vals[STAGED ? kTopkCap : 4];
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_scan[NT / kWave + 1];
-  __shared__ uint32_t s_res[4];
+  constexpr int kChunk = NT * E;
+  const int tid = threadIdx.x;
+  const int base = vec ? (lo & ~3) : lo;
+  const int nchunks = RESIDENT ? 1 : (hi - base + kChunk - 1) / kChunk;
 
+  uint32_t raw[E], key[E];
+  uint32_t vmask = 0;   // bit e: element e lies in [lo, hi)
+  auto load = [&](int c0) {
+    const int p0 = c0 + tid * E;
+    if (vec) {
+#pragma unroll
+      for (int v = 0; v < E / 4; ++v) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p0 + 4 * v < hi) x = *reinterpret_cast<const float4*>(src + p0 + 4 * v);
+        raw[4 * v] = __float_as_uint(x.x);
+        raw[4 * v + 1] = __float_as_uint(x.y);
+        raw[4 * v + 2] = __float_as_uint(x.z);
+        raw[4 * v + 3] = __float_as_uint(x.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) raw[e] = (p0 + e < hi) ? __float_as_uint(src[p0 + e]) : 0u;
+    }
+    vmask = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = p0 + e >= lo && p0 + e < hi;
+      vmask |= ok ? (1u << e) : 0u;
+      key[e] = order_key(raw[e]);
+    }
+  };
+  // runs f(c0) for every chunk with raw/key/vmask holding that chunk
+  auto sweep = [&](auto f) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int c0 = base + c * kChunk;
+      if (!RESIDENT) load(c0);
+      f(c0);
+    }
+  };
+
+  // ---- 1. min / max of the finite valid scores -----------------------------
+  if (RESIDENT) load(base);
+  float vmin = INFINITY, vmax = -INFINITY;
+  sweep([&](int) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = ((vmask >> e) & 1u) && finite_bits(raw[e]);
+      const float x = __uint_as_float(raw[e]);
+      vmin = fminf(vmin, ok ? x : INFINITY);
+      vmax = fmaxf(vmax, ok ? x : -INFINITY);
+    }
+  });
+  clear_words<NT>(sm.hist[0], kBins);
+  if (tid == 0) sm.cnt = 0;
+  block_min_max<NT>(vmin, vmax, sm.red);
+  const LinBins lb = make_lin_bins(vmin, vmax);
+
+  // ---- 2. threshold key ---------------------------------------------------
+  sweep([&](int) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      atomicAdd(&sm.hist[0][lin_bin(raw[e], lb)], (vmask >> e) & 1u);
+  });
+  __syncthreads();
+  const Bucket bk = block_find_bucket<true>(sm.hist[0], kBins, (uint32_t)k, sm.res);
+  uint32_t kt, take;
+  if (bk.count <= (uint32_t)kTopkListCap) {
+    sweep([&](int) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (((vmask >> e) & 1u) && lin_bin(raw[e], lb) == bk.bin) {
+          const uint32_t slot = atomicAdd(&sm.cnt, 1u);
+          sm.list[slot] = key[e];   // slot < count <= the list capacity
+        }
+      }
+    });
+    __syncthreads();
+    list_threshold<NT>(sm.list, (int)bk.count, bk.need, sm.res);
+    kt = sm.res[0];
+    take = sm.res[1];
+  } else {
+    uint32_t n_kt;
+    radix_threshold<NT>(sm.hist, sm.res, (uint32_t)k, [&](auto f) {
+      sweep([&](int) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) f(key[e], ((vmask >> e) & 1u) != 0u);
+      });
+    }, &kt, &take, &n_kt);
+  }
+
+  // ---- 3. stable compaction in position order -----------------------------
+  uint32_t run_gt = 0, run_eq = 0;
+  int chunk = 0;
+  sweep([&](int c0) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = (vmask >> e) & 1u;
+      gt += (ok && key[e] > kt) ? 1u : 0u;
+      eq += (ok && key[e] == kt) ? 1u : 0u;
+    }
+    uint32_t total;   // packed counts: a chunk holds <= 16K elements < 2^16
+    const uint32_t excl = block_scan_excl<NT>(gt | (eq << 16), sm.scan[chunk & 1], total);
+    uint32_t g_before = run_gt + (excl & 0xffffu);
+    uint32_t e_before = run_eq + (excl >> 16);
+    const int l0 = c0 + tid * E;
+    int gq = l0 / I, gm = l0 - (l0 / I) * I;   // l = gq * I + gm, walked without division
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = (vmask >> e) & 1u;
+      const bool is_gt = ok && key[e] > kt;
+      const bool is_eq = ok && key[e] == kt;
+      const uint32_t pos = g_before + (e_before < take ? e_before : take);
+      if ((is_gt || (is_eq && e_before < take)) && pos < (uint32_t)k) {
+        sm.out[pos] = make_float2(__uint_as_float(raw[e]), (float)((gq * S + r) * I + gm));
+        sm.idx[pos] = l0 + e;
+      }
+      g_before += is_gt ? 1u : 0u;
+      e_before += is_eq ? 1u : 0u;
+      if (++gm == I) { gm = 0; ++gq; }
+    }
+    run_gt += total & 0xffffu;
+    run_eq += total >> 16;
+    ++chunk;
+  });
+  __syncthreads();
+
+  // ---- 4. coalesced write-out (exactly k selections) ----------------------
+  if (ocand) {
+    if (out_vec) {
+      for (int i = tid; i < k / 2; i += NT)
+        reinterpret_cast<float4*>(ocand)[i] = reinterpret_cast<const float4*>(sm.out)[i];
+    } else {
+      for (int i = tid; i < k; i += NT) ocand[i] = sm.out[i];
+    }
+  }
+  if (oidx) {
+    for (int i = tid; i < k; i += NT) oidx[i] = sm.idx[i];
+  }
+}
+
+template <int E>
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
+    const float* __restrict__ logits, int64_t ld, int64_t shard_stride, int rows, int ctx,
+    const int* __restrict__ row_starts, const int* __restrict__ row_ends, int k, int S, int I,
+    int shard_first, int* __restrict__ local_idx, float* __restrict__ cand, int vec4,
+    int cand_vec) {
+  __shared__ TopkSmem sm;
+  constexpr int NT = kTopkThreads;
   const int row = blockIdx.x;
   const int j = blockIdx.y;
   const int r = shard_first + j;
@@ -60,152 +217,50 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
   float2* ocand =
       cand ? reinterpret_cast<float2*>(cand) + ((int64_t)row * S + r) * k : nullptr;
 
-  auto emit = [&](int pos, int l, uint32_t bits) {
-    if (oidx) oidx[pos] = l;
-    if (ocand) ocand[pos] = make_float2(__uint_as_float(bits), (float)global_of(r, l, S, I));
-  };
-
   if (n <= k) {  // everything valid is selected
     for (int i = tid; i < k; i += NT) {
+      int l = -1;
+      float2 c = make_float2(-INFINITY, -1.0f);
       if (i < n) {
-        emit(i, lo + i, __float_as_uint(src[lo + i]));
-      } else {
-        if (oidx) oidx[i] = -1;
-        if (ocand) ocand[i] = make_float2(-INFINITY, -1.0f);
+        l = lo + i;
+        c = make_float2(src[l], (float)global_of(r, l, S, I));
       }
+      if (oidx) oidx[i] = l;
+      if (ocand) ocand[i] = c;
     }
     return;
   }
-
-  auto val = [&](int i) -> uint32_t {
-    if constexpr (STAGED) return s_vals[i];
-    else return __float_as_uint(src[lo + i]);
-  };
-
-  // ---- 1. stage + first-digit histogram ---------------------------------
-  clear_hist<NT>(s_hist, kBins);
-  __syncthreads();
-  if (STAGED && vec4) {
-    const float4* src4 = reinterpret_cast<const float4*>(src);
-    for (int v = (lo >> 2) + tid; (v << 2) < hi; v += NT) {
-      const float4 x = src4[v];
-      const uint32_t b[4] = {__float_as_uint(x.x), __float_as_uint(x.y),
-                             __float_as_uint(x.z), __float_as_uint(x.w)};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = (v << 2) + q;
-        if (e >= lo && e < hi) {
-          if constexpr (STAGED) s_vals[e - lo] = b[q];
-          atomicAdd(&s_hist[order_key(b[q]) >> 21], 1u);
-        }
-      }
-    }
-  } else {
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t b = __float_as_uint(src[lo + i]);
-      if constexpr (STAGED) s_vals[i] = b;
-      atomicAdd(&s_hist[order_key(b) >> 21], 1u);
-    }
-  }
-  __syncthreads();
-
-  // ---- 2. find the threshold prefix --------------------------------------
-  Bucket bk = find_bucket<NT, true>(s_hist, kBins, (uint32_t)k, s_scan, s_res);
-  uint32_t prefix = bk.bin;
-  int shift = 21;
-  if (bk.count != bk.need) {
-    clear_hist<NT>(s_hist, kBins);
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t key = order_key(val(i));
-      if ((key >> 21) == prefix) atomicAdd(&s_hist[(key >> 10) & 0x7ffu], 1u);
-    }
-    __syncthreads();
-    bk = find_bucket<NT, true>(s_hist, kBins, bk.need, s_scan, s_res);
-    prefix = (prefix << 11) | bk.bin;
-    shift = 10;
-    if (bk.count != bk.need) {
-      clear_hist<NT>(s_hist, 1024);
-      __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t key = order_key(val(i));
-        if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 0x3ffu], 1u);
-      }
-      __syncthreads();
-      bk = find_bucket<NT, true>(s_hist, 1024, bk.need, s_scan, s_res);
-      prefix = (prefix << 10) | bk.bin;
-      shift = 0;
-    }
-  }
-  const uint32_t need = bk.need;
-
-  // ---- 3. stable compaction in position order ----------------------------
-  constexpr int kTile = NT * kTopkIpt;
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < n; base += kTile) {
-    const int e0 = base + tid * kTopkIpt;
-    uint32_t bits[kTopkIpt];
-    bool loaded = false;
-    if constexpr (STAGED) {
-      if (e0 + kTopkIpt <= n) {
-        const uint4 v4 = *reinterpret_cast<const uint4*>(&s_vals[e0]);
-        bits[0] = v4.x; bits[1] = v4.y; bits[2] = v4.z; bits[3] = v4.w;
-        loaded = true;
-      }
-    }
-    if (!loaded) {
-#pragma unroll
-      for (int q = 0; q < kTopkIpt; ++q) bits[q] = (e0 + q < n) ? val(e0 + q) : 0u;
-    }
-    uint32_t gt = 0, eq = 0;
-    uint32_t pk[kTopkIpt];
-#pragma unroll
-    for (int q = 0; q < kTopkIpt; ++q) {
-      pk[q] = order_key(bits[q]) >> shift;
-      const bool in = e0 + q < n;
-      gt += (in && pk[q] > prefix) ? 1u : 0u;
-      eq += (in && pk[q] == prefix) ? 1u : 0u;
-    }
-    uint32_t total;
-    const uint32_t excl = block_excl_scan<NT>(gt | (eq << 16), s_scan, total);
-    uint32_t g_before = run_gt + (excl & 0xffffu);
-    uint32_t e_before = run_eq + (excl >> 16);
-#pragma unroll
-    for (int q = 0; q < kTopkIpt; ++q) {
-      if (e0 + q >= n) break;
-      if (pk[q] > prefix) {
-        const uint32_t pos = g_before + (e_before < need ? e_before : need);
-        if (pos < (uint32_t)k) emit((int)pos, lo + e0 + q, bits[q]);
-        ++g_before;
-      } else if (pk[q] == prefix) {
-        if (e_before < need) {
-          const uint32_t pos = g_before + e_before;
-          if (pos < (uint32_t)k) emit((int)pos, lo + e0 + q, bits[q]);
-        }
-        ++e_before;
-      }
-    }
-    run_gt += total & 0xffffu;
-    run_eq += total >> 16;
-  }
+  // 16-byte loads start at the aligned position at or below lo; when that
+  // would push a row that fits one chunk past it, the row is loaded
+  // element-wise instead
+  constexpr int kChunk = NT * E;
+  const bool vec = vec4 && (hi - (lo & ~3) <= kChunk || n > kChunk);
+  const int span = hi - (vec ? (lo & ~3) : lo);
+  if (span <= kChunk)
+    topk_row<E, true>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0);
+  else
+    topk_row<E, false>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0);
 }
 
-int launch_topk_select(const float* logits, int64_t ld, int64_t shard_stride, int rows,
-                       int ctx, const int* row_starts, const int* row_ends, int k,
-                       int S, int I, int shard_first, int shard_count, int* local_idx,
-                       float* cand, hipStream_t stream) {
+int launch_topk_select(const float* logits, int64_t ld, int64_t shard_stride, int rows, int ctx,
+                       const int* row_starts, const int* row_ends, int k, int S, int I,
+                       int shard_first, int shard_count, int* local_idx, float* cand,
+                       hipStream_t stream) {
   const int max_local = local_count(ctx, shard_first, S, I);
-  const bool vec4 = ((uintptr_t)logits % 16 == 0) && (ld % 4 == 0) && (shard_stride % 4 == 0);
+  const int vec4 =
+      ((uintptr_t)logits % 16 == 0) && (ld % 4 == 0) && (shard_stride % 4 == 0) ? 1 : 0;
+  const int cand_vec = ((uintptr_t)cand % 16 == 0) ? 1 : 0;   // k is even
   dim3 grid(rows, shard_count);
-  if (max_local <= kTopkCap) {
-    hipLaunchKernelGGL(topk_select_kernel<true>, grid, dim3(kTopkThreads), 0, stream, logits,
-                       ld, shard_stride, rows, ctx, row_starts, row_ends, k, S, I,
-                       shard_first, local_idx, cand, vec4 ? 1 : 0);
-  } else {
-    hipLaunchKernelGGL(topk_select_kernel<false>, grid, dim3(kTopkThreads), 0, stream, logits,
-                       ld, shard_stride, rows, ctx, row_starts, row_ends, k, S, I,
-                       shard_first, local_idx, cand, vec4 ? 1 : 0);
-  }
+  // rows of up to 8K local positions are held 8 per thread, longer ones 16
+  // per thread (swept in 16K chunks beyond 16K)
+  if (max_local <= kTopkThreads * 8)
+    hipLaunchKernelGGL((topk_select_kernel<8>), grid, dim3(kTopkThreads), 0, stream, logits, ld,
+                       shard_stride, rows, ctx, row_starts, row_ends, k, S, I, shard_first,
+                       local_idx, cand, vec4, cand_vec);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<16>), grid, dim3(kTopkThreads), 0, stream, logits,
+                       ld, shard_stride, rows, ctx, row_starts, row_ends, k, S, I, shard_first,
+                       local_idx, cand, vec4, cand_vec);
   return 0;
 }
 

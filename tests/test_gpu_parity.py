@@ -216,3 +216,52 @@ def test_native_library_is_loaded():
     with open("/proc/self/maps") as f:
         maps = f.read()
     assert os.path.realpath(dsa.LIB_PATH) in maps or dsa.LIB_PATH in maps
+
+
+@pytest.mark.parametrize("cache_dtype,splits", [("bf16", 1), ("bf16", 2), ("fp8", 1)])
+def test_attention_score_jump_restarts_exactly(cache_dtype, splits):
+    """The kernel fixes its softmax reference max from the first tile; a later
+    tile whose scores exceed it by more than 2^64 (base 2) makes the workgroup
+    restart its token list.  Scores here jump by ~77 (base 2) after the first
+    three tiles, with distinct values among the high rows, so the result is
+    only right if the restart path is."""
+    from oracle.formats import f64_to_bf16, f64_to_e4m3
+    rng = np.random.default_rng(7)
+    R, H, P, k = 2, 128, 1, 512
+    nslots = 8 * 64
+    vals = np.zeros((nslots, 576))
+    vals[:, :512] = rng.standard_normal((nslots, 512))          # values
+    order = rng.permutation(nslots)
+    cnt = 300
+    late = order[100:cnt]                                         # tiles 3.. of the list
+    vals[late, 512:] = 2.5 + 0.05 * rng.standard_normal((len(late), 64))
+    scale = 2.0 ** -4
+    if cache_dtype == "fp8":
+        cache = f64_to_e4m3(vals / scale).reshape(8, 64, 576)
+        cache_t = torch.from_numpy(cache).cuda()
+        cs = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    else:
+        cache = f64_to_bf16(vals).reshape(8, 64, 576)
+        cache_t = torch.from_numpy(cache.view(np.int16)).cuda().view(torch.bfloat16)
+        cs = None
+    qv = np.zeros((R, H, 576))
+    qv[:, :, 512:] = 8.0 * (1 + np.arange(H) / 512.0)[None, :, None]
+    qb = f64_to_bf16(qv)
+    slots = np.full((P, R, k), -1, np.int32)
+    counts = np.zeros((P, R), np.int32)
+    for i in range(R):
+        slots[0, i, :cnt] = order[:cnt] if i == 0 else order[cnt - 1::-1][:cnt]
+        counts[0, i] = cnt
+    sm = float(np.float32(1 / 24))
+    out, lse = dsa.sparse_mla_decode(
+        torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16), cache_t,
+        torch.from_numpy(slots).cuda(), torch.from_numpy(counts).cuda(), sm_scale=sm,
+        splits=splits, cache_scale=cs)
+    torch.cuda.synchronize()
+    gpo = bf16_bits_to_f64(bits16(out))
+    gpl = lse.cpu().numpy().astype(np.float64)
+    gpo, gpl = split_partials_to_parts(gpo, gpl, P, splits)
+    opo, opl = oracle.sparse_mla_partial(qb, cache, cache_dtype, scale if cache_dtype == "fp8" else 1.0,
+                                         slots, counts, sm)
+    bad = attn_mismatch(gpo, opo, gpl, opl)
+    assert not bad, bad

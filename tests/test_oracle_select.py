@@ -143,6 +143,20 @@ def test_convert_round_trip(S, I):
                 assert slots[0, i, j] == bt[0, i, g // B] * B + g % B
 
 
+def test_convert_guards_rows_and_columns_outside_the_table():
+    # a request outside the table keeps nothing; a block column past the
+    # table width is dropped, the rest keep their order
+    S, I, B = 1, 1, 4
+    bt = np.array([[[7, 3]]], np.int32)            # one request, two blocks
+    ids = np.array([[1, 6, 9, -1], [0, 1, 2, 3]], np.int32)
+    slots, counts = oracle.convert_index(ids, np.array([0, 3], np.int32), bt, B, S, I)
+    assert slots[0, 0].tolist() == [7 * 4 + 1, 3 * 4 + 2, -1, -1]   # id 9: column 2 >= 2
+    assert counts[0].tolist() == [2, 0]
+    assert slots[0, 1].tolist() == [-1, -1, -1, -1]
+    slots, counts = oracle.convert_index(ids[:1], np.array([-1], np.int32), bt, B, S, I)
+    assert counts[0].tolist() == [0]
+
+
 # ---- planted mistakes ------------------------------------------------------
 def test_planted_tie_break_mistake_is_caught(monkeypatch):
     def wrong_order(scores, ids):                 # ties by descending id
