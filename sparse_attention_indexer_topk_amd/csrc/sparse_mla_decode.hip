@@ -19,10 +19,14 @@
 //    all 128 heads;
 //  - the part's slot list is staged once in LDS; the selected latent rows are
 //    gathered 32 tokens per tile straight from HBM into LDS with
-//    global_load_lds_dwordx4 (no register staging) through a 3-stage ring:
-//    tile t+1 is in flight while tile t is consumed, and a stage is reused
-//    only after the barrier that follows its last reader; two barriers per
-//    tile (tile arrival, score exchange);
+//    global_load_lds_dwordx4 (no register staging; a uniform base plus a
+//    32-bit offset per lane when the pool spans less than 4 GiB) through a
+//    3-stage ring: tiles t+1 and t+2 are in flight while tile t is consumed,
+//    and a stage is reused only after the barrier that follows its last
+//    reader; two barriers per tile (tile arrival, score exchange);
+//  - the value fragments of output block mb+1 are read while the MFMAs of
+//    block mb run, and the score k-steps are left to the compiler's
+//    scheduler, so that LDS latency overlaps MFMA work;
 //  - the 16-byte chunks of a row are XOR-swizzled (swz_key) so that both the
 //    score-operand reads and the value transpose reads are free of bank
 //    conflicts;
@@ -43,7 +47,9 @@
 //    with the hardware converter (exact: e4m3 is a subset of bf16); the
 //    per-tensor scale is folded into the score scale and the output;
 //  - split-K: `splits` workgroups share a part's token list, each emitting its
-//    own partial; lse_combine merges them like shards.
+//    own partial; lse_combine merges them like shards;
+//  - the epilogue stages each wave's normalised outputs in LDS and stores them
+//    as 16-byte lanes covering whole 512-byte row halves.
 #include "launchers.h"
 
 namespace dsa {
@@ -73,6 +79,11 @@ constexpr int kMaxSel = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartSlack = 64.0f;         // log2 units
+// epilogue staging: each wave's 32 heads x 256 bf16 outputs, rows padded by
+// 8 bytes so that the row-strided 8-byte writes spread over the banks
+constexpr int kEpiRow = kValue + 8;            // bytes per staged row (256 bf16 + pad)
+constexpr int kEpiWaveB = kHPW * kEpiRow;
+constexpr int kEpiB = kAttnWaves * kEpiWaveB;
 
 // DMA instructions (64 lanes x 16 B) per tile, dealt round-robin to the waves
 constexpr int kDmaBf16Total = kTileB / (16 * kWave);           // 36
@@ -94,7 +105,7 @@ __device__ __forceinline__ int swz_key(int t) {
 }
 __device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ swz_key(t)) << 4); }
 
-template <bool FP8>
+template <bool FP8, bool OFF32>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
     const float* __restrict__ cache_scale, int64_t num_slots, const int* __restrict__ slots,
@@ -103,11 +114,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   constexpr int kRingB = FP8 ? kTileB8 : kTileB;
   constexpr int kDmaTotal = FP8 ? kDmaFp8Total : kDmaBf16Total;
   constexpr int kDmaMax = (kDmaTotal + kAttnWaves - 1) / kAttnWaves;
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kStages][kRingB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_conv[FP8 ? kTileB : 16];
-  __shared__ __attribute__((aligned(16))) float4 s_x[kAttnWaves][4][kWave];  // score partials
+  constexpr int kConvB = FP8 ? kTileB : 0;
+  constexpr int kXB = kAttnWaves * 4 * kWave * 16;
+  constexpr int kMainB = kStages * kRingB + kConvB + kXB;
+  constexpr int kSmemB = kMainB > kEpiB ? kMainB : kEpiB;
+  __shared__ __attribute__((aligned(16))) uint8_t s_main[kSmemB];
   __shared__ int s_slot[kMaxSel];
   __shared__ int s_restart;
+  uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
+  uint8_t* s_conv = s_main + kStages * kRingB;
+  float4 (*s_x)[4][kWave] =
+      reinterpret_cast<float4 (*)[4][kWave]>(s_main + kStages * kRingB + kConvB);
 
   const int row = blockIdx.x;
   const int part = blockIdx.y / splits;
@@ -145,7 +162,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const float kv_scale = FP8 ? cache_scale[0] : 1.0f;
   const float qk_scale = sm_scale * kv_scale * kLog2e;
 
-  // q fragments: head `head`, features 288*u + 16*kk + 8*g .. +8
+  // q fragments: head `head`, features 288*u + 16*kk + 8*g .. +8 (in flight
+  // while the first tiles are requested)
   bf16x8_t qf[kQSteps];
   {
     const uint16_t* qp =
@@ -164,7 +182,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
   float m_ref = -INFINITY, l_part = 0.f;
   if (tid == 0) s_restart = 0;
-  __syncthreads();   // slot list and flag ready
+  lgkm_wait0();
+  bar();   // slot list and flag ready (q may still be in flight)
 
   // ---- lane-invariant LDS byte offsets inside a bf16 tile -------------------
   // scores: k-step kk of member u reads logical chunk 36u + g + 2kk of token
@@ -192,21 +211,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 
   // ---- DMA issue of tile tt into its ring stage -------------------------------
   // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
-  // instructions are dealt round-robin to the waves.
-  int dma_to[kDmaMax];
-#pragma unroll
-  for (int jj = 0; jj < kDmaMax; ++jj) {
-    const int p = (jj * kAttnWaves + wave) * kWave + lane;
-    int t, off;
-    if constexpr (FP8) {
-      t = p / (kRowB8 / 16);
-      off = (p % (kRowB8 / 16)) * 16;
-    } else {
-      t = p / kRowChunks;
-      off = ((p % kRowChunks) ^ swz_key(t)) * 16;
-    }
-    dma_to[jj] = (t & 31) | (off << 8);
-  }
+  // instructions are dealt round-robin to the waves.  With OFF32 the source is
+  // the uniform cache base plus a 32-bit byte offset (one VGPR per lane).
   auto issue = [&](int tt) {
     uint8_t* stage = s_ring[tt % kStages];
     const int tbase = tt * kTile;
@@ -214,10 +220,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
       if (ins < kDmaTotal) {
-        const int t = dma_to[jj] & 31;
+        const int p = ins * kWave + lane;
+        int t, off;
+        if constexpr (FP8) {
+          t = p / (kRowB8 / 16);
+          off = (p % (kRowB8 / 16)) * 16;
+        } else {
+          t = p / kRowChunks;
+          off = ((p % kRowChunks) ^ swz_key(t)) * 16;
+        }
         const int ti = tbase + t < n_tok ? tbase + t : 0;
         const int s = max(s_slot[ti], 0);
-        const uint8_t* src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + (dma_to[jj] >> 8);
+        const uint8_t* src;
+        if constexpr (OFF32)
+          src = cache + (uint32_t)((uint32_t)s * (uint32_t)(FP8 ? kRowB8 : kRowB) + (uint32_t)off);
+        else
+          src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + off;
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (lds_void_ptr)(stage + ins * kWave * 16), 16, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -227,17 +245,20 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // this wave's DMA instructions per tile
   const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  // Iteration tt issues tile tt+1 into the stage tile tt-2 used (free since
-  // the previous iteration's first barrier), waits for tile tt and computes
-  // it.  A restart request raised while computing tile tt is seen at the next
+  // Tiles 0 and 1 are requested before the loop; iteration tt waits for tile
+  // tt, passes the barrier (after which every wave is done with tile tt-1),
+  // requests tile tt+2 into tile tt-1's stage and computes tile tt.  A
+  // restart request raised while computing tile tt is seen at the next
   // barrier: inside the loop at the next tile's arrival barrier, after the
   // last tile at the barrier below the loop.
-  int next_issue = 0;
   int tt = 0;
+  int next_issue = 0;
   for (;;) {
   for (; tt < ntiles;) {
+    // stages of tiles <= tt+1 are free before this barrier (only at the start
+    // or after a restart is anything left to request here)
     while (next_issue < ntiles && next_issue <= tt + 1) issue(next_issue++);
-    if (next_issue - 1 > tt) {
+    if (tt + 1 < ntiles) {
       if (my_dma == 5) vm_wait<5>();
       else if (my_dma == 4) vm_wait<4>();
       else if (my_dma == 3) vm_wait<3>();
@@ -263,6 +284,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       next_issue = 0;
       continue;
     }
+    if (next_issue < ntiles) issue(next_issue++);   // tile tt+2, into tile tt-1's stage
 
     const uint8_t* tile = s_ring[tt % kStages];
     if constexpr (FP8) {
@@ -307,7 +329,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         const bf16x8_t a =
             *reinterpret_cast<const bf16x8_t*>(tile + qk_off[kk & 3] + 128 * (kk >> 2));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
-        if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
@@ -366,12 +387,19 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         return __builtin_bit_cast(bf16x8_t,
                                   __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
+      bf16x8_t va0 = vfrag(0, 0), va1 = vfrag(0, 1);
 #pragma unroll
       for (int mb = 0; mb < kOBlocks; ++mb) {
-        const bf16x8_t va0 = vfrag(mb, 0), va1 = vfrag(mb, 1);
+        bf16x8_t nb0 = va0, nb1 = va1;
+        if (mb + 1 < kOBlocks) {   // next block's fragments in flight during these MFMAs
+          nb0 = vfrag(mb + 1, 0);
+          nb1 = vfrag(mb + 1, 1);
+        }
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pf0, o[mb], 0, 0, 0);
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pf1, o[mb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        va0 = nb0;
+        va1 = nb1;
       }
     }
     ++tt;
@@ -392,24 +420,38 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
 
   // ---- epilogue ---------------------------------------------------------------
+  // Each wave stages its 32 heads x 256 normalised bf16 outputs row-major in
+  // LDS (the tile ring is free: every wave passed the barrier after the last
+  // tile), then stores them with 16-byte lanes, two 512-byte row halves per
+  // instruction.
+  const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
+  const float inv = l_tot > 0.f ? kv_scale / l_tot : 0.f;
+  uint8_t* stg = s_main + wave * kEpiWaveB;
   if (pair_on) {
-    const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
-    if (head_on) {
-      const float inv = l_tot > 0.f ? kv_scale / l_tot : 0.f;
-      uint16_t* op =
-          out + (((int64_t)out_part * rows + row) * heads + head) * kValue + 256 * u + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < kOBlocks; ++mb)
+    for (int mb = 0; mb < kOBlocks; ++mb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint2 v = make_uint2(pack_bf16x2(o[mb][4 * b] * inv, o[mb][4 * b + 1] * inv),
-                                     pack_bf16x2(o[mb][4 * b + 2] * inv, o[mb][4 * b + 3] * inv));
-          *reinterpret_cast<uint2*>(op + 32 * mb + 8 * b) = v;
-        }
-      if (g == 0 && u == 0) {
-        const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-        lse[((int64_t)out_part * rows + row) * heads + head] = lv;
+      for (int b = 0; b < 4; ++b) {
+        const uint2 v = make_uint2(pack_bf16x2(o[mb][4 * b] * inv, o[mb][4 * b + 1] * inv),
+                                   pack_bf16x2(o[mb][4 * b + 2] * inv, o[mb][4 * b + 3] * inv));
+        *reinterpret_cast<uint2*>(stg + j32 * kEpiRow + (32 * mb + 8 * b + 4 * g) * 2) = v;
       }
+  }
+  lgkm_wait0();   // a wave reads back only what it wrote itself
+  if (pair_on) {
+    uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue + 256 * u;
+    const int half = lane >> 5, col = (lane & 31) * 16;
+#pragma unroll
+    for (int i = 0; i < kHPW / 2; ++i) {
+      const int r = 2 * i + half;
+      if (h0 + r < heads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kEpiRow + col);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + col) = v;
+      }
+    }
+    if (head_on && g == 0 && u == 0) {
+      const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      lse[((int64_t)out_part * rows + row) * heads + head] = lv;
     }
   }
 }
@@ -422,15 +464,20 @@ int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cac
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cache);
   uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
+  // 32-bit gather offsets when the whole pool lies within 4 GiB of its base
+  const bool off32 = num_slots * (int64_t)(fp8 ? kRowB8 : kRowB) <= (int64_t)0xffffffffLL;
+#define DSA_ATTN(F, O)                                                                       \
+  hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O>), grid, dim3(kAttnThreads), 0, stream,   \
+                     q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits,  \
+                     sm_scale, o16, lse)
   if (fp8) {
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, grid, dim3(kAttnThreads), 0, stream, q16,
-                       rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits, sm_scale,
-                       o16, lse);
+    if (off32) DSA_ATTN(true, true);
+    else DSA_ATTN(true, false);
   } else {
-    hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, grid, dim3(kAttnThreads), 0, stream, q16,
-                       rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits, sm_scale,
-                       o16, lse);
+    if (off32) DSA_ATTN(false, true);
+    else DSA_ATTN(false, false);
   }
+#undef DSA_ATTN
   return 0;
 }
 
