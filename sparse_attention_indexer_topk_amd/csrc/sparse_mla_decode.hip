@@ -9,32 +9,25 @@
 //   lse = ln sum_j exp(s_j).
 //
 // How (gfx950, one workgroup = 8 waves = 128 heads of one (row, part, split)):
-//  - waves work in pairs; a pair owns 32 heads.  Member u of a pair computes
-//    the partial scores over features [288u, 288u + 288) with q in VGPRs as
-//    the B operand of v_mfma_f32_32x32x16_bf16 (18 k-steps, 72 VGPRs); the
-//    pair swaps its fp32 partials through LDS so both hold the full scores,
-//    then member u accumulates output features [256u, 256u + 256) (8 blocks
-//    of 32 x 32 fp32 = 128 accumulators).  That keeps a wave under 256
-//    registers (two waves per SIMD) while the key tile enters LDS once for
-//    all 128 heads;
+//  - each wave owns 16 heads over all 576 features: q (the B operand of
+//    v_mfma_f32_16x16x32_bf16, 18 k-steps) stays in 72 VGPRs and the output
+//    (32 blocks of 16 x 16 fp32) in 128, so waves need no partial-score
+//    exchange and the key tile enters LDS once for all 128 heads;
 //  - the part's slot list is staged once in LDS; the selected latent rows are
 //    gathered 32 tokens per tile straight from HBM into LDS with
 //    global_load_lds_dwordx4 (no register staging; a uniform base plus a
 //    32-bit offset per lane when the pool spans less than 4 GiB) through a
-//    3-stage ring: tiles t+1 and t+2 are in flight while tile t is consumed,
-//    and a stage is reused only after the barrier that follows its last
-//    reader; two barriers per tile (tile arrival, score exchange);
-//  - the value fragments of output block mb+1 are read while the MFMAs of
-//    block mb run, and the score k-steps are left to the compiler's
-//    scheduler, so that LDS latency overlaps MFMA work;
+//    4-stage ring with tiles t+1 and t+2 in flight while tile t is consumed;
+//    one barrier per tile (tile arrival, which also retires tile t-1);
 //  - the 16-byte chunks of a row are XOR-swizzled (swz_key) so that both the
-//    score-operand reads and the value transpose reads are free of bank
-//    conflicts;
-//  - scores are computed transposed, S^T = K Q^T (rows = tokens), so the
-//    accumulator gives each lane 16 tokens of ONE head — exactly the B
-//    operand (P^T) of the value product O^T += V^T P^T;
-//  - V^T fragments are read from the same row-major tile with
-//    ds_read_b64_tr_b16 (LDS transpose read): no transposed copy of V;
+//    score-operand reads (16 rows x one chunk) and the value transpose reads
+//    (4 rows x 32 bytes per 16 lanes) are free of bank conflicts;
+//  - scores are computed transposed, S^T = K Q^T (rows = tokens), so each
+//    lane ends with 8 tokens of ONE head — with the token order inside the
+//    k dimension permuted the same way on both operands, exactly the B
+//    operand (P^T) of the value product O^T += V^T P^T; V^T fragments are
+//    read from the row-major tile with ds_read_b64_tr_b16 (LDS transpose
+//    read), the next block's while the current block's MFMA runs;
 //  - softmax in base 2 (v_exp_f32 computes 2^x) against a reference max
 //    fixed by the first tile: probabilities may exceed 1 by up to 2^64, which
 //    fp32 accumulators and bf16 operands hold exactly as well as values near
@@ -48,15 +41,15 @@
 //    per-tensor scale is folded into the score scale and the output;
 //  - split-K: `splits` workgroups share a part's token list, each emitting its
 //    own partial; lse_combine merges them like shards;
-//  - the epilogue stages each wave's normalised outputs in LDS and stores them
-//    as 16-byte lanes covering whole 512-byte row halves.
+//  - the epilogue stages each wave's normalised outputs in LDS and stores one
+//    whole 1 KB head row per instruction.
 #include "launchers.h"
 
 namespace dsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -64,24 +57,24 @@ typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / kWave;   // 8
-constexpr int kHPW = 32;                       // heads per wave pair
-constexpr int kHPB = kHPW * kAttnWaves / 2;    // heads per block (128)
+constexpr int kHPW = 16;                       // heads per wave
+constexpr int kHPB = kHPW * kAttnWaves;        // heads per block (128)
 constexpr int kTile = 32;                      // tokens per tile
-constexpr int kStages = 3;                     // tiles in the LDS ring
+constexpr int kStages = 4;                     // tiles in the LDS ring
 constexpr int kRowB = kLatent * 2;             // bf16 row bytes (1152)
 constexpr int kRowChunks = kRowB / 16;         // 72 16-byte chunks
 constexpr int kTileB = kTile * kRowB;          // 36864 bytes
 constexpr int kRowB8 = kLatent;                // fp8 row bytes (576)
 constexpr int kTileB8 = kTile * kRowB8;        // 18432 bytes
-constexpr int kQSteps = kLatent / 16 / 2;      // 18 per pair member
-constexpr int kOBlocks = kValue / 32 / 2;      // 8 per pair member
+constexpr int kQSteps = kLatent / 32;          // 18 k-steps of 32 features
+constexpr int kOBlocks = kValue / 16;          // 32 blocks of 16 output features
 constexpr int kMaxSel = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartSlack = 64.0f;         // log2 units
-// epilogue staging: each wave's 32 heads x 256 bf16 outputs, rows padded by
-// 8 bytes so that the row-strided 8-byte writes spread over the banks
-constexpr int kEpiRow = kValue + 8;            // bytes per staged row (256 bf16 + pad)
+// epilogue staging: each wave's 16 heads x 512 bf16 outputs, rows padded by
+// 16 bytes so that the row-strided 8-byte writes spread over the banks
+constexpr int kEpiRow = kValue * 2 + 16;
 constexpr int kEpiWaveB = kHPW * kEpiRow;
 constexpr int kEpiB = kAttnWaves * kEpiWaveB;
 
@@ -96,10 +89,24 @@ __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void vm_wait_n(int n) {
+  switch (n) {
+    case 0: vm_wait<0>(); break;
+    case 2: vm_wait<2>(); break;
+    case 3: vm_wait<3>(); break;
+    case 4: vm_wait<4>(); break;
+    case 5: vm_wait<5>(); break;
+    case 6: vm_wait<6>(); break;
+    case 8: vm_wait<8>(); break;
+    case 10: vm_wait<10>(); break;
+    default: vm_wait<0>(); break;   // any other count: wait for everything
+  }
+}
 __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
-// byte offset of logical 16-byte chunk c of token row t inside a bf16 tile
+// XOR key of the 16-byte chunks of token row t inside a tile (depends on the
+// row's low 4 bits); chunk_off gives the byte offset of logical chunk c
 __device__ __forceinline__ int swz_key(int t) {
   return ((t >> 1) & 1) | (((t ^ (t >> 2)) & 1) << 1) | (((t ^ (t >> 1) ^ (t >> 3)) & 1) << 2);
 }
@@ -115,16 +122,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   constexpr int kDmaTotal = FP8 ? kDmaFp8Total : kDmaBf16Total;
   constexpr int kDmaMax = (kDmaTotal + kAttnWaves - 1) / kAttnWaves;
   constexpr int kConvB = FP8 ? kTileB : 0;
-  constexpr int kXB = kAttnWaves * 4 * kWave * 16;
-  constexpr int kMainB = kStages * kRingB + kConvB + kXB;
+  constexpr int kMainB = kStages * kRingB + kConvB;
   constexpr int kSmemB = kMainB > kEpiB ? kMainB : kEpiB;
   __shared__ __attribute__((aligned(16))) uint8_t s_main[kSmemB];
   __shared__ int s_slot[kMaxSel];
   __shared__ int s_restart;
   uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
   uint8_t* s_conv = s_main + kStages * kRingB;
-  float4 (*s_x)[4][kWave] =
-      reinterpret_cast<float4 (*)[4][kWave]>(s_main + kStages * kRingB + kConvB);
 
   const int row = blockIdx.x;
   const int part = blockIdx.y / splits;
@@ -132,14 +136,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int hg = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int pair = wave >> 1;
-  const int u = wave & 1;         // pair member: feature half
   const int lane = lane_id();
-  const int j32 = lane & 31;      // head column / token row of 32x32 operands
-  const int g = lane >> 5;        // k-group of 32x32 operands
-  const int h0 = hg * kHPB + pair * kHPW;
-  const int head = h0 + j32;
-  const bool pair_on = h0 < heads;
+  const int n16 = lane & 15;      // head column of the 16x16 operands
+  const int g4 = lane >> 4;       // k-group of the 16x16x32 operands
+  const int h0 = hg * kHPB + wave * kHPW;
+  const int head = h0 + n16;
+  const bool wave_on = h0 < heads;
   const bool head_on = head < heads;
   const int out_part = blockIdx.y;
 
@@ -162,51 +164,41 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const float kv_scale = FP8 ? cache_scale[0] : 1.0f;
   const float qk_scale = sm_scale * kv_scale * kLog2e;
 
-  // q fragments: head `head`, features 288*u + 16*kk + 8*g .. +8 (in flight
-  // while the first tiles are requested)
+  // q fragments (B operand of S^T = K Q^T): head `head`, features
+  // 32*kk + 8*g4 .. +8 (in flight while the first tiles are requested)
   bf16x8_t qf[kQSteps];
   {
-    const uint16_t* qp =
-        q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 288 * u + 8 * g;
+    const uint16_t* qp = q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 8 * g4;
 #pragma unroll
     for (int kk = 0; kk < kQSteps; ++kk) {
-      u16x8_t v = *reinterpret_cast<const u16x8_t*>(qp + 16 * kk);
+      u16x8_t v = *reinterpret_cast<const u16x8_t*>(qp + 32 * kk);
       if (!head_on) v = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
       qf[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  f32x16_t o[kOBlocks];
+  f32x4_t o[kOBlocks];
 #pragma unroll
-  for (int mb = 0; mb < kOBlocks; ++mb)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+  for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
   if (tid == 0) s_restart = 0;
   lgkm_wait0();
   bar();   // slot list and flag ready (q may still be in flight)
 
   // ---- lane-invariant LDS byte offsets inside a bf16 tile -------------------
-  // scores: k-step kk of member u reads logical chunk 36u + g + 2kk of token
-  // row j32 -> qk_off[kk % 4] + 128 * (kk / 4)
-  int qk_off[4];
+  // scores: k-step kk reads token row tb + n16 (tb = 0, 16), logical chunk
+  // 4kk + g4; the key of rows n16 and 16 + n16 is the same and only touches
+  // the low 3 chunk bits, so the offset is qk_off[kk % 2] + 128 * (kk / 2)
+  int qk_off[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) qk_off[i] = chunk_off(j32, 36 * u + g + 2 * i);
-  // values (transpose reads): 16-lane group G = lane/16 has k-group g = G/2
-  // and feature half fs = G%2; inside it, source role sp = lane%16 reads
-  // token row 16*ks + 8*h + 4*g + sp/4 at features 256u + 32mb + 16fs +
-  // 4(sp%4) -> pv_off[mb % 2][h] + 16*ks*row + 128*(mb/2) (the swizzle key is
-  // linear and ignores row bit 4, so only h changes the per-lane base)
-  int pv_off[2][2];
-  {
-    const int sp = lane & 15, fs = (lane >> 4) & 1;
-    const int trb = 4 * g + (sp >> 2);
+  for (int p = 0; p < 2; ++p) qk_off[p] = chunk_off(n16, 4 * p + g4);
+  // values (transpose reads): in 16-lane group g4, source lane s = n16 reads
+  // token row 4*g4 + s/4 (+16 for the second read) at features 16*fb + 4*(s%4);
+  // logical chunk 2fb + (s%4)/2, so the offset is pv_off[fb % 4] + 128*(fb/4)
+  int pv_off[4];
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int feat = 256 * u + 32 * par + 16 * fs + 4 * (sp & 3);
-        pv_off[par][h] = chunk_off(trb + 8 * h, feat >> 3) + (feat & 7) * 2;
-      }
+  for (int p = 0; p < 4; ++p) {
+    const int r = 4 * g4 + (n16 >> 2);
+    pv_off[p] = chunk_off(r, 2 * p + ((n16 & 3) >> 1)) + 8 * (n16 & 1);
   }
 
   // ---- DMA issue of tile tt into its ring stage -------------------------------
@@ -245,27 +237,110 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // this wave's DMA instructions per tile
   const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  // Tiles 0 and 1 are requested before the loop; iteration tt waits for tile
-  // tt, passes the barrier (after which every wave is done with tile tt-1),
-  // requests tile tt+2 into tile tt-1's stage and computes tile tt.  A
-  // restart request raised while computing tile tt is seen at the next
-  // barrier: inside the loop at the next tile's arrival barrier, after the
-  // last tile at the barrier below the loop.
+  // ---- one tile: scores, softmax, values -------------------------------------
+  auto compute = [&](int tt) {
+    const uint8_t* tile = FP8 ? s_conv : s_ring[tt % kStages];
+    const int tbase = tt * kTile;
+    const uint32_t vmask = (uint32_t)__ballot(lane < kTile && tbase + lane < n_tok &&
+                                              s_slot[tbase + (lane & 31)] >= 0);
+    if (!wave_on) return;
+    // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kQSteps; ++kk) {
+      const uint8_t* a = tile + qk_off[kk & 1] + 128 * (kk >> 1);
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 16 * kRowB);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
+    }
+    // lane holds head `head`, tokens 4*g4 + i (s0) and 16 + 4*g4 + i (s1)
+    if (vmask != 0xffffffffu) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!((vmask >> (4 * g4 + i)) & 1u)) s0[i] = -INFINITY;
+        if (!((vmask >> (16 + 4 * g4 + i)) & 1u)) s1[i] = -INFINITY;
+      }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * qk_scale;
+    if (m_ref == -INFINITY) {
+      m_ref = mt;
+    } else if (__any(mt > m_ref + kRestartSlack)) {
+      m_ref = fmaxf(m_ref, mt);
+      if (lane == 0) s_restart = 1;
+    }
+    const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    // P^T operand: element e < 4 is token 4*g4 + e, element 4 + e is token
+    // 16 + 4*g4 + e (the value fragments below use the same token order)
+    bf16x8_t pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], qk_scale, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], qk_scale, nm));
+      l_part += p0;
+      l_part += p1;
+      pf[i] = static_cast<__bf16>(p0);
+      pf[4 + i] = static_cast<__bf16>(p1);
+    }
+    // O^T += V^T P^T, 16 output features per block: ds_read_b64_tr_b16 gives
+    // lane (g4, n16) element e = V[token 4*g4 + e (+16)][16*fb + n16]
+    auto vfrag = [&](int fb) {
+      const uint8_t* b = tile + pv_off[fb & 3] + 128 * (fb >> 2);
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 16 * kRowB));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t va = vfrag(0);
+#pragma unroll
+    for (int fb = 0; fb < kOBlocks; ++fb) {
+      bf16x8_t nb = va;
+      if (fb + 1 < kOBlocks) nb = vfrag(fb + 1);   // next block's fragment in flight
+      o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[fb], 0, 0, 0);
+      if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      va = nb;
+    }
+  };
+
+  // fp8: widen raw tile tt into the swizzled bf16 layout of s_conv
+  auto widen = [&](int tt) {
+    if constexpr (FP8) {
+      const uint8_t* raw8 = s_ring[tt % kStages];
+      for (int c = tid; c < kTileB8 / 16; c += kAttnThreads) {
+        const int tr = c / (kRowB8 / 16);
+        const int c8 = c % (kRowB8 / 16);            // features 16*c8 .. +16
+        const uint4 rw = *reinterpret_cast<const uint4*>(raw8 + c * 16);
+        const uint32_t w[4] = {rw.x, rw.y, rw.z, rw.w};
+        uint32_t h[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, false);
+          const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, true);
+          h[2 * q4] = __builtin_bit_cast(uint32_t, lo);
+          h[2 * q4 + 1] = __builtin_bit_cast(uint32_t, hi);
+        }
+        *reinterpret_cast<uint4*>(s_conv + chunk_off(tr, 2 * c8)) =
+            make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(s_conv + chunk_off(tr, 2 * c8 + 1)) =
+            make_uint4(h[4], h[5], h[6], h[7]);
+      }
+    }
+  };
+
+  // Iteration tt requests tiles up to tt+2 (tile tt+2 goes to the stage of
+  // tile tt-2, which every wave left before the previous barrier), waits for
+  // tile tt, passes the barrier (every wave is then done with tile tt-1) and
+  // computes tile tt.  A restart request raised while computing tile tt is
+  // seen at the next barrier: inside the loop at the next tile's barrier,
+  // after the last tile at the barrier below the loop.
   int tt = 0;
   int next_issue = 0;
   for (;;) {
   for (; tt < ntiles;) {
-    // stages of tiles <= tt+1 are free before this barrier (only at the start
-    // or after a restart is anything left to request here)
-    while (next_issue < ntiles && next_issue <= tt + 1) issue(next_issue++);
-    if (tt + 1 < ntiles) {
-      if (my_dma == 5) vm_wait<5>();
-      else if (my_dma == 4) vm_wait<4>();
-      else if (my_dma == 3) vm_wait<3>();
-      else vm_wait<2>();
-    } else {
-      vm_wait<0>();
-    }
+    while (next_issue < ntiles && next_issue <= tt + 2) issue(next_issue++);
+    vm_wait_n(my_dma * (next_issue - 1 - tt));
     lgkm_wait0();
     bar();   // tile tt visible; every wave is done with tile tt-1
     if (s_restart) {
@@ -275,133 +350,19 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       bar();
       if (tid == 0) s_restart = 0;
 #pragma unroll
-      for (int mb = 0; mb < kOBlocks; ++mb)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+      for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_part = 0.f;
       __syncthreads();
       tt = 0;
       next_issue = 0;
       continue;
     }
-    if (next_issue < ntiles) issue(next_issue++);   // tile tt+2, into tile tt-1's stage
-
-    const uint8_t* tile = s_ring[tt % kStages];
     if constexpr (FP8) {
-      // widen to the swizzled bf16 layout: 1152 chunks of 16 codes
-      for (int c = tid; c < kTileB8 / 16; c += kAttnThreads) {
-        const int t = c / (kRowB8 / 16);
-        const int c8 = c % (kRowB8 / 16);            // features 16*c8 .. +16
-        const uint4 raw = *reinterpret_cast<const uint4*>(tile + c * 16);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t h[8];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, false);
-          const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, true);
-          h[2 * q4] = __builtin_bit_cast(uint32_t, lo);
-          h[2 * q4 + 1] = __builtin_bit_cast(uint32_t, hi);
-        }
-        *reinterpret_cast<uint4*>(s_conv + chunk_off(t, 2 * c8)) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(s_conv + chunk_off(t, 2 * c8 + 1)) =
-            make_uint4(h[4], h[5], h[6], h[7]);
-      }
+      widen(tt);
       lgkm_wait0();
       bar();
-      tile = s_conv;
     }
-
-    // token validity of this tile as a wave-uniform bit mask
-    const int tbase = tt * kTile;
-    const uint64_t vmask =
-        __ballot(lane < kTile && tbase + lane < n_tok && s_slot[tbase + (lane & 31)] >= 0);
-
-    // ---- partial S^T = K Q^T over this member's 288 features -----------------
-    f32x16_t sacc;
-#pragma unroll
-    for (int a = 0; a < 16; ++a) sacc[a] = 0.f;
-    if (pair_on) {
-      // k-step kk reads logical chunk c0 + 2*kk of token row j32; the swizzle
-      // only permutes the low 3 chunk bits, so the address is one of 4
-      // per-lane bases (kk % 4) plus 128 bytes per 4 k-steps
-#pragma unroll
-      for (int kk = 0; kk < kQSteps; ++kk) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(tile + qk_off[kk & 3] + 128 * (kk >> 2));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-        s_x[wave][a4][lane] = make_float4(sacc[4 * a4], sacc[4 * a4 + 1], sacc[4 * a4 + 2],
-                                          sacc[4 * a4 + 3]);
-    }
-    lgkm_wait0();
-    bar();                                           // partials visible
-    if (pair_on) {
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 x = s_x[wave ^ 1][a4][lane];
-        sacc[4 * a4] += x.x;
-        sacc[4 * a4 + 1] += x.y;
-        sacc[4 * a4 + 2] += x.z;
-        sacc[4 * a4 + 3] += x.w;
-      }
-      // lane holds head `head`, tokens 8*(a/4) + 4*g + a%4 (same in both members)
-      if (vmask != 0xffffffffull) {
-        const uint32_t vm = (uint32_t)(vmask >> (4 * g));
-#pragma unroll
-        for (int a = 0; a < 16; ++a)
-          if (!((vm >> (8 * (a >> 2) + (a & 3))) & 1u)) sacc[a] = -INFINITY;
-      }
-      float mt = sacc[0];
-#pragma unroll
-      for (int a = 1; a < 16; ++a) mt = fmaxf(mt, sacc[a]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * qk_scale;
-      if (m_ref == -INFINITY) {
-        m_ref = mt;
-      } else if (__any(mt > m_ref + kRestartSlack)) {
-        m_ref = fmaxf(m_ref, mt);
-        if (lane == 0) s_restart = 1;
-      }
-      const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      bf16x8_t pf0, pf1;   // probabilities, rounded to nearest even by the hardware
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[a], qk_scale, nm));
-        l_part += p;
-        if (a < 8) pf0[a] = static_cast<__bf16>(p);
-        else pf1[a - 8] = static_cast<__bf16>(p);
-      }
-
-      // ---- O^T += V^T P^T over this member's 256 output features --------------
-      // V^T fragments come from the row-major tile through ds_read_b64_tr_b16:
-      // 16-lane group G = lane/16 has k-group g = G/2 and feature half fs = G%2;
-      // inside it, source role sp = lane%16 addresses token row
-      // 8*(2*ks + h) + 4*g + sp/4 at features f + 16*fs + 4*(sp%4).
-      auto vfrag = [&](int mb, int ks) {
-        s16x4_t v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(
-              tile + pv_off[mb & 1][h] + 16 * ks * kRowB + 128 * (mb >> 1)));
-        return __builtin_bit_cast(bf16x8_t,
-                                  __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8_t va0 = vfrag(0, 0), va1 = vfrag(0, 1);
-#pragma unroll
-      for (int mb = 0; mb < kOBlocks; ++mb) {
-        bf16x8_t nb0 = va0, nb1 = va1;
-        if (mb + 1 < kOBlocks) {   // next block's fragments in flight during these MFMAs
-          nb0 = vfrag(mb + 1, 0);
-          nb1 = vfrag(mb + 1, 1);
-        }
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0, pf0, o[mb], 0, 0, 0);
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1, pf1, o[mb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        va0 = nb0;
-        va1 = nb1;
-      }
-    }
+    compute(tt);
     ++tt;
   }
   lgkm_wait0();
@@ -410,9 +371,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   bar();
   if (tid == 0) s_restart = 0;
 #pragma unroll
-  for (int mb = 0; mb < kOBlocks; ++mb)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) o[mb][a] = 0.f;
+  for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   l_part = 0.f;
   __syncthreads();
   tt = 0;
@@ -420,36 +379,32 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  // Each wave stages its 32 heads x 256 normalised bf16 outputs row-major in
-  // LDS (the tile ring is free: every wave passed the barrier after the last
-  // tile), then stores them with 16-byte lanes, two 512-byte row halves per
-  // instruction.
-  const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
+  // Each wave stages its 16 heads x 512 normalised bf16 outputs row-major in
+  // LDS (the ring is free: every wave passed the barrier after the last tile),
+  // then stores one whole 1 KB head row per instruction.
+  float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
   const float inv = l_tot > 0.f ? kv_scale / l_tot : 0.f;
   uint8_t* stg = s_main + wave * kEpiWaveB;
-  if (pair_on) {
+  if (wave_on) {
 #pragma unroll
-    for (int mb = 0; mb < kOBlocks; ++mb)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint2 v = make_uint2(pack_bf16x2(o[mb][4 * b] * inv, o[mb][4 * b + 1] * inv),
-                                   pack_bf16x2(o[mb][4 * b + 2] * inv, o[mb][4 * b + 3] * inv));
-        *reinterpret_cast<uint2*>(stg + j32 * kEpiRow + (32 * mb + 8 * b + 4 * g) * 2) = v;
-      }
+    for (int fb = 0; fb < kOBlocks; ++fb) {
+      const uint2 v = make_uint2(pack_bf16x2(o[fb][0] * inv, o[fb][1] * inv),
+                                 pack_bf16x2(o[fb][2] * inv, o[fb][3] * inv));
+      *reinterpret_cast<uint2*>(stg + n16 * kEpiRow + (16 * fb + 4 * g4) * 2) = v;
+    }
   }
   lgkm_wait0();   // a wave reads back only what it wrote itself
-  if (pair_on) {
-    uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue + 256 * u;
-    const int half = lane >> 5, col = (lane & 31) * 16;
+  if (wave_on) {
+    uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue;
 #pragma unroll
-    for (int i = 0; i < kHPW / 2; ++i) {
-      const int r = 2 * i + half;
+    for (int r = 0; r < kHPW; ++r) {
       if (h0 + r < heads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kEpiRow + col);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + col) = v;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kEpiRow + lane * 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + lane * 16) = v;
       }
     }
-    if (head_on && g == 0 && u == 0) {
+    if (head_on && g4 == 0) {
       const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       lse[((int64_t)out_part * rows + row) * heads + head] = lv;
     }

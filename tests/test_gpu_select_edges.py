@@ -14,7 +14,11 @@ an id range needing several bitmap sweeps.
 
 Convert: rows whose request is outside the table.
 
-Every result is compared element by element (bit for bit) with the oracle.
+Every selection result is compared element by element (bit for bit) with the
+oracle.
+
+Attention: a bf16 pool larger than 4 GiB (the 64-bit gather addresses),
+against the oracle to the attention tolerance.
 """
 import sys
 
@@ -249,3 +253,43 @@ def test_convert_rows_outside_table():
     torch.cuda.synchronize()
     assert np.array_equal(gs.cpu().numpy(), es)
     assert np.array_equal(gc.cpu().numpy(), ec)
+
+
+# ------------------------------------------------------------ attention --
+def test_attention_pool_beyond_4gib_bf16():
+    """A bf16 pool larger than 4 GiB gathers with 64-bit addresses; rows near
+    its end and near its start must both be read right."""
+    from dsa_testlib import attn_mismatch, bf16_bits_to_f64  # noqa: F401
+    n_slots = (1 << 32) // 1152 + 40_000            # just past 4 GiB of bf16 rows
+    R, H, k = 2, 32, 512
+    r = np.random.default_rng(21)
+    counts = np.array([[k, 300]], np.int32)
+    slots = np.full((1, R, k), -1, np.int32)
+    for i in range(R):
+        c = counts[0, i]
+        hi = r.choice(np.arange(n_slots - 60_000, n_slots), size=c // 2, replace=False)
+        lo = r.choice(60_000, size=c - c // 2, replace=False)
+        slots[0, i, :c] = np.concatenate([hi, lo])
+    used = np.unique(slots[slots >= 0])
+    rows_bits = (r.standard_normal((len(used), 576)).astype(np.float32)
+                 .view(np.uint32) >> 16).astype(np.uint16)          # bf16 by truncation
+    q = (r.standard_normal((R, H, 576)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    log(f"attention pool {n_slots} slots ({n_slots * 1152 / 2**30:.2f} GiB)")
+    cache = torch.empty((n_slots, 576), dtype=torch.int16, device=DEV)
+    cache[torch.from_numpy(used.astype(np.int64)).to(DEV)] = \
+        torch.from_numpy(rows_bits.view(np.int16)).to(DEV)
+    sm_scale = float(np.float32(1.0 / 24.0))
+    out, lse = dsa.sparse_mla_decode(torch.from_numpy(q.view(np.int16)).to(DEV).view(torch.bfloat16),
+                                     cache.view(torch.bfloat16),
+                                     torch.from_numpy(slots).to(DEV),
+                                     torch.from_numpy(counts).to(DEV), sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    # the oracle sees only the used rows, with the slots renumbered
+    remap = {int(s): j for j, s in enumerate(used)}
+    oslots = np.vectorize(lambda s: remap.get(int(s), -1))(slots).astype(np.int32)
+    po, pl = oracle.sparse_mla_partial(q, rows_bits, "bf16", None, oslots, counts, sm_scale)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    del cache
+    torch.cuda.empty_cache()
+    bad = attn_mismatch(bf16_bits_to_f64(got), po, lse.cpu().numpy(), pl)
+    assert not bad, bad
