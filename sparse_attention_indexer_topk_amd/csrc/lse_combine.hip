@@ -7,15 +7,25 @@
 // A (row, head) whose partials are all empty gets out = 0, lse = -inf.
 //
 // How: a pure streaming kernel — one thread per (row, head, 8 features),
-// 16-byte loads of the partials four at a time, fp32 accumulation in
-// partial order, 16-byte bf16 store.
+// fp32 accumulation in partial order, 16-byte bf16 store.  With at most 8
+// partials every load (the partial LSEs and the 16-byte output slices) is
+// issued before the first is used, so a thread makes one memory round trip;
+// more partials are taken four at a time.
 #include "launchers.h"
 
 namespace dsa {
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineFast = 8;   // partials held in registers at once
 constexpr float kLog2eC = 1.4426950408889634f;
 
+__device__ __forceinline__ void accumulate8(float (&acc)[8], float w, const uint4 v) {
+  const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] += w * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+}
+
+template <bool FAST>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
     const uint16_t* __restrict__ pout, const float* __restrict__ plse, int P, int64_t rh_total,
     int dim, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
@@ -24,35 +34,56 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
   if (gid >= rh_total * chunks) return;
   const int64_t rh = gid / chunks;
   const int c = (int)(gid % chunks);
+  auto slice = [&](int p) {
+    return reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
+  };
 
-  float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, plse[(int64_t)p * rh_total + rh]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  if (M != -INFINITY) {
-    // partials in batches of four: all four loads are in flight together
-    constexpr int B = 4;
-    for (int p0 = 0; p0 < P; p0 += B) {
-      uint4 v[B];
-      float w[B];
+  float z = 0.f, M = -INFINITY;
+  if constexpr (FAST) {
+    float l[kCombineFast];
+    uint4 v[kCombineFast];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int p = p0 + b;
-        w[b] = 0.f;
-        v[b] = make_uint4(0u, 0u, 0u, 0u);
-        if (p < P) {
-          w[b] = exp2f((plse[(int64_t)p * rh_total + rh] - M) * kLog2eC);  // exp(-inf) = 0
-          v[b] = *reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
-        }
+    for (int p = 0; p < kCombineFast; ++p) {
+      l[p] = -INFINITY;
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (p < P) {
+        l[p] = plse[(int64_t)p * rh_total + rh];
+        v[p] = *slice(p);
       }
+    }
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        z += w[b];
-        if (w[b] == 0.f) continue;   // an empty partial contributes nothing, whatever it holds
-        const uint32_t ws[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+    for (int p = 0; p < kCombineFast; ++p) M = fmaxf(M, l[p]);
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[e] += w[b] * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+      for (int p = 0; p < kCombineFast; ++p) {
+        const float w = exp2f((l[p] - M) * kLog2eC);   // exp(-inf) = 0
+        z += w;
+        if (w != 0.f) accumulate8(acc, w, v[p]);          // an empty partial adds nothing
+      }
+    }
+  } else {
+    for (int p = 0; p < P; ++p) M = fmaxf(M, plse[(int64_t)p * rh_total + rh]);
+    if (M != -INFINITY) {
+      constexpr int B = 4;
+      for (int p0 = 0; p0 < P; p0 += B) {
+        uint4 v[B];
+        float w[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int p = p0 + b;
+          w[b] = 0.f;
+          v[b] = make_uint4(0u, 0u, 0u, 0u);
+          if (p < P) {
+            w[b] = exp2f((plse[(int64_t)p * rh_total + rh] - M) * kLog2eC);
+            v[b] = *slice(p);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          z += w[b];
+          if (w[b] != 0.f) accumulate8(acc, w[b], v[b]);
+        }
       }
     }
   }
@@ -70,9 +101,14 @@ int launch_lse_combine(const void* part_out, const float* part_lse, int P, int r
   const int64_t rh = (int64_t)rows * heads;
   const int64_t threads = rh * (dim / 8);
   const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
-  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
-                     stream, reinterpret_cast<const uint16_t*>(part_out), part_lse, P, rh, dim,
-                     reinterpret_cast<uint16_t*>(out), lse_out);
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(part_out);
+  uint16_t* o = reinterpret_cast<uint16_t*>(out);
+  if (P <= kCombineFast)
+    hipLaunchKernelGGL(lse_combine_kernel<true>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
+                       stream, po, part_lse, P, rh, dim, o, lse_out);
+  else
+    hipLaunchKernelGGL(lse_combine_kernel<false>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
+                       stream, po, part_lse, P, rh, dim, o, lse_out);
   return 0;
 }
 

@@ -208,31 +208,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   auto issue = [&](int tt) {
     uint8_t* stage = s_ring[tt % kStages];
     const int tbase = tt * kTile;
+    // all of this wave's slot reads first (one LDS round trip), then the DMAs
+    int sv[kDmaMax], offv[kDmaMax];
+#pragma unroll
+    for (int jj = 0; jj < kDmaMax; ++jj) {
+      const int ins = jj * kAttnWaves + wave;
+      sv[jj] = 0;
+      offv[jj] = 0;
+      if (ins < kDmaTotal) {
+        const int p = ins * kWave + lane;
+        int t;
+        if constexpr (FP8) {
+          t = p / (kRowB8 / 16);
+          offv[jj] = (p % (kRowB8 / 16)) * 16;
+        } else {
+          t = p / kRowChunks;
+          offv[jj] = ((p % kRowChunks) ^ swz_key(t)) * 16;
+        }
+        const int ti = tbase + t < n_tok ? tbase + t : 0;
+        sv[jj] = s_slot[ti];
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
       if (ins < kDmaTotal) {
-        const int p = ins * kWave + lane;
-        int t, off;
-        if constexpr (FP8) {
-          t = p / (kRowB8 / 16);
-          off = (p % (kRowB8 / 16)) * 16;
-        } else {
-          t = p / kRowChunks;
-          off = ((p % kRowChunks) ^ swz_key(t)) * 16;
-        }
-        const int ti = tbase + t < n_tok ? tbase + t : 0;
-        const int s = max(s_slot[ti], 0);
+        const int s = max(sv[jj], 0);
         const uint8_t* src;
         if constexpr (OFF32)
-          src = cache + (uint32_t)((uint32_t)s * (uint32_t)(FP8 ? kRowB8 : kRowB) + (uint32_t)off);
+          src = cache + (uint32_t)((uint32_t)s * (uint32_t)(FP8 ? kRowB8 : kRowB) + (uint32_t)offv[jj]);
         else
-          src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + off;
+          src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + offv[jj];
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (lds_void_ptr)(stage + ins * kWave * 16), 16, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // this wave's DMA instructions per tile
   const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
