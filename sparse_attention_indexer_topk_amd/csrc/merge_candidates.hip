@@ -115,6 +115,10 @@ __device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict
     }
   });
   clear_words<NT>(sm.hist[0], kBins);
+  {   // the first bitmap sweep's words, cleared here behind the loads
+    const int span0 = id_bound < kIdChunk ? id_bound : kIdChunk;
+    for (int w = tid; w < (span0 + 31) >> 5; w += NT) sm.bitmap[w] = 0u;
+  }
   if (tid == 0) {
     sm.cnt = 0;
     sm.nvalid = 0;
@@ -183,13 +187,7 @@ __device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict
           }
         });
         __syncthreads();
-        if (tid < (int)n_kt) {
-          const uint32_t mine = sm.list[tid];
-          uint32_t below = 0;
-          for (int j = 0; j < (int)n_kt; ++j) below += sm.list[j] < mine ? 1u : 0u;
-          if (below == take - 1) sm.res[3] = mine;
-        }
-        __syncthreads();
+        list_kth_smallest<NT>(sm.list, (int)n_kt, take, &sm.res[3]);
         id_thr = sm.res[3];
       } else {
         uint32_t need = take, id_prefix = 0;
@@ -228,8 +226,10 @@ __device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict
     const int span = (id_bound - b0) < kIdChunk ? (id_bound - b0) : kIdChunk;
     const int nwords = (span + 31) >> 5;
     const int wpt = (nwords + NT - 1) / NT;   // words per thread, <= kIdWordsPerThread
-    for (int w = tid; w < nwords; w += NT) sm.bitmap[w] = 0u;
-    __syncthreads();
+    if (b0 > 0) {   // later sweeps clear the words the previous sweep used
+      for (int w = tid; w < nwords; w += NT) sm.bitmap[w] = 0u;
+      __syncthreads();
+    }
     sweep([&]() {
 #pragma unroll
       for (int e = 0; e < E; ++e) {

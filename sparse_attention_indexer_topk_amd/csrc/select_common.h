@@ -154,15 +154,26 @@ __device__ __forceinline__ bool finite_bits(uint32_t bits) {
   return (bits & 0x7f800000u) != 0x7f800000u;
 }
 
+// Max over the 64 lanes of a wave, left in every lane: DPP row shifts and
+// row broadcasts build an inclusive max-scan (lanes outside a row read
+// -inf), lane 63 holds the wave's max.
+__device__ __forceinline__ float wave_max(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowShr1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowShr2, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowShr4, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowShr8, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowBcast15, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), kDppRowBcast31, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
 // Min and max over the block; `scratch` holds 2 * NT/64 floats.  One barrier.
 template <int NT>
 __device__ __forceinline__ void block_min_max(float& vmin, float& vmax, float* scratch) {
   constexpr int NW = NT / kWave;
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) {
-    vmin = fminf(vmin, __shfl_xor(vmin, d, kWave));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, d, kWave));
-  }
+  vmax = wave_max(vmax);
+  vmin = -wave_max(-vmin);
   const int wave = threadIdx.x / kWave;
   if (lane_id() == 0) {
     scratch[wave] = vmin;
@@ -176,29 +187,63 @@ __device__ __forceinline__ void block_min_max(float& vmin, float& vmax, float* s
   }
 }
 
-// Exact threshold among the `c` order keys in `list` (c <= NT): the
-// `need`-th largest key kt, and how many elements equal to kt are taken
-// (need minus the keys above kt).  The thread holding a key with
-// (#keys above) < need <= (#keys at or above) publishes the pair; all such
-// threads hold kt and write the same words.  One barrier; the result is in
-// res[0] (kt), res[1] (take) and res[2] (how many keys equal kt).
+// Exact threshold among the `c` (<= 128) order keys in `list`: the
+// `need`-th largest key kt, how many elements equal to kt are taken (need
+// minus the keys above kt), and how many keys equal kt.  Wave 0 holds the
+// list in its lanes (two keys per lane) and compares every pair through
+// readlane broadcasts; the lane holding a key with (#keys above) < need <=
+// (#keys at or above) publishes the result (several such lanes hold the same
+// kt and write the same words).  One barrier; the result is in res[0] (kt),
+// res[1] (take) and res[2] (how many keys equal kt).
 template <int NT>
 __device__ __forceinline__ void list_threshold(const uint32_t* list, int c, uint32_t need,
                                                uint32_t* res) {
-  const int tid = threadIdx.x;
-  if (tid < c) {
-    const uint32_t kx = list[tid];
-    uint32_t above = 0, at_least = 0;
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    const uint32_t k0 = lane < c ? list[lane] : 0u;
+    const uint32_t k1 = lane + kWave < c ? list[lane + kWave] : 0u;
+    uint32_t a0 = 0, g0 = 0, a1 = 0, g1 = 0;   // above / at-least counts of k0 and k1
     for (int j = 0; j < c; ++j) {
-      const uint32_t kj = list[j];
-      above += kj > kx ? 1u : 0u;
-      at_least += kj >= kx ? 1u : 0u;
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane(
+          (int)(j < kWave ? k0 : k1), j & (kWave - 1));
+      a0 += kj > k0 ? 1u : 0u;
+      g0 += kj >= k0 ? 1u : 0u;
+      a1 += kj > k1 ? 1u : 0u;
+      g1 += kj >= k1 ? 1u : 0u;
     }
-    if (above < need && need <= at_least) {
-      res[0] = kx;
-      res[1] = need - above;
-      res[2] = at_least - above;   // how many keys equal kt
+    if (lane < c && a0 < need && need <= g0) {
+      res[0] = k0;
+      res[1] = need - a0;
+      res[2] = g0 - a0;
     }
+    if (lane + kWave < c && a1 < need && need <= g1) {
+      res[0] = k1;
+      res[1] = need - a1;
+      res[2] = g1 - a1;
+    }
+  }
+  __syncthreads();
+}
+
+// The `kth`-smallest (1-based) of the `c` (<= 128) DISTINCT values in
+// `list`, written to *res by the lane holding it; wave 0 compares all pairs
+// through readlane broadcasts.  One barrier.
+template <int NT>
+__device__ __forceinline__ void list_kth_smallest(const uint32_t* list, int c, uint32_t kth,
+                                                  uint32_t* res) {
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    const uint32_t v0 = lane < c ? list[lane] : 0u;
+    const uint32_t v1 = lane + kWave < c ? list[lane + kWave] : 0u;
+    uint32_t b0 = 0, b1 = 0;   // how many values lie below v0 / v1
+    for (int j = 0; j < c; ++j) {
+      const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane(
+          (int)(j < kWave ? v0 : v1), j & (kWave - 1));
+      b0 += vj < v0 ? 1u : 0u;
+      b1 += vj < v1 ? 1u : 0u;
+    }
+    if (lane < c && b0 + 1 == kth) *res = v0;
+    if (lane + kWave < c && b1 + 1 == kth) *res = v1;
   }
   __syncthreads();
 }
