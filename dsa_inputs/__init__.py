@@ -70,6 +70,7 @@ class Spec:
     prologue: bool = False          # fp8 workload: new K rows + insert
     fp8_scale: float = 2.0 ** -4
     q_pos_step: int = 1             # causal: row i ends at 1 + i*step
+    q_len: int = 1                  # query tokens per request (multi-token decode)
 
 
 CONFIGS = {
@@ -108,6 +109,10 @@ PARITY_CASES = {
     "fp8_bf16pro_s": Spec("fp8_bf16pro_s", rows=3, ctx=3333, shards=2,
                           interleave=3, k=1024, heads=16, seed=17,
                           prologue=True, latent_std=1.0),
+    # multi-token decode: 3 requests x 3 query tokens sharing each request's
+    # block table; 2 shards, as in the pages' [4, 4, 5] localisation example
+    "mtp_s": Spec("mtp_s", rows=9, ctx=9001, shards=2, interleave=1, k=512,
+                  heads=16, seed=18, q_len=3),
 }
 
 
@@ -259,6 +264,14 @@ def _row_bounds(sp: Spec, rng):
         # full rows, a row shorter than k, a row of one token, mid lengths
         choices = [C, max(1, sp.k // 2 + 3), 1, C // 3 + 7, C - 5]
         ends = np.array([choices[i % len(choices)] for i in range(R)], dtype=np.int64)
+    if sp.q_len > 1:
+        # multi-token decode: request r has global length L_r; its j-th of
+        # q_len query tokens sees L_r - (q_len - 1 - j) tokens (the per-token
+        # lengths are expanded globally, then localised per shard)
+        n_req = R // sp.q_len
+        base = np.maximum(C - 37 * np.arange(n_req, dtype=np.int64), sp.q_len)
+        i = np.arange(R, dtype=np.int64)
+        ends = base[i // sp.q_len] - (sp.q_len - 1 - i % sp.q_len)
     starts = np.zeros(R, dtype=np.int64)
     if sp.row_starts == "window":
         starts = np.array([(i * 97) % max(1, C // 4) for i in range(R)], dtype=np.int64)
@@ -318,7 +331,7 @@ def make(name_or_spec, *, with_cache: bool = True) -> Case:
     ld = sharded.shape[-1]
     q = _draw_bf16_normal(rng, (R, H, D_LATENT), 1.0)
 
-    Rq = 1 if sp.one_request else R
+    Rq = 1 if sp.one_request else R // sp.q_len
     W = -(-ld // BLOCK)                       # table width per (shard, request)
     nblocks = S * Rq * W
     if with_cache:
@@ -332,7 +345,8 @@ def make(name_or_spec, *, with_cache: bool = True) -> Case:
         cache = np.zeros((0, BLOCK, D_LATENT), dtype=np.uint8 if sp.cache == "fp8" else np.uint16)
         scale = np.float32(sp.fp8_scale if sp.cache == "fp8" else 1.0)
     block_table = rng.permutation(nblocks).astype(np.int32).reshape(S, Rq, W)
-    row_req = np.zeros(R, dtype=np.int32) if sp.one_request else np.arange(R, dtype=np.int32)
+    row_req = (np.zeros(R, dtype=np.int32) if sp.one_request
+               else (np.arange(R, dtype=np.int32) // sp.q_len).astype(np.int32))
 
     case = Case(spec=sp, global_logits=g, logits=sharded, row_starts=starts,
                 row_ends=ends, row_req=row_req, q=q, cache=cache,
