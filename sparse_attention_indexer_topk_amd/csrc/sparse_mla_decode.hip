@@ -19,9 +19,11 @@
 //    32-bit offset per lane when the pool spans less than 4 GiB) through a
 //    4-stage ring with tiles t+1 and t+2 in flight while tile t is consumed;
 //    one barrier per tile (tile arrival, which also retires tile t-1);
-//  - the 16-byte chunks of a row are XOR-swizzled (swz_key) so that both the
-//    score-operand reads (16 rows x one chunk) and the value transpose reads
-//    (4 rows x 32 bytes per 16 lanes) are free of bank conflicts;
+//  - the gather lays a tile out in LDS as 36 blocks of 16 tokens x 32
+//    features (tile_off): a score k-step reads one contiguous 1 KB block and a
+//    value transpose read 512 contiguous bytes, free of the bank conflicts
+//    that strided row reads meet on this LDS; one gather instruction fills
+//    one block;
 //  - scores are computed transposed, S^T = K Q^T (rows = tokens), so each
 //    lane ends with 8 tokens of ONE head — with the token order inside the
 //    k dimension permuted the same way on both operands, exactly the B
@@ -62,7 +64,6 @@ constexpr int kHPB = kHPW * kAttnWaves;        // heads per block (128)
 constexpr int kTile = 32;                      // tokens per tile
 constexpr int kStages = 4;                     // tiles in the LDS ring
 constexpr int kRowB = kLatent * 2;             // bf16 row bytes (1152)
-constexpr int kRowChunks = kRowB / 16;         // 72 16-byte chunks
 constexpr int kTileB = kTile * kRowB;          // 36864 bytes
 constexpr int kRowB8 = kLatent;                // fp8 row bytes (576)
 constexpr int kTileB8 = kTile * kRowB8;        // 18432 bytes
@@ -105,12 +106,15 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
-// XOR key of the 16-byte chunks of token row t inside a tile (depends on the
-// row's low 4 bits); chunk_off gives the byte offset of logical chunk c
-__device__ __forceinline__ int swz_key(int t) {
-  return ((t >> 1) & 1) | (((t ^ (t >> 2)) & 1) << 1) | (((t ^ (t >> 1) ^ (t >> 3)) & 1) << 2);
+// Tile layout in LDS: 36 blocks of 1 KB, block (c / 4) * 2 + t / 16 holding
+// tokens 16*(t/16) .. +16 x 16-byte chunks 4*(c/4) .. +4 (32 features), slot
+// (t % 16) + 16 * (c % 4) inside the block.  A score k-step then reads one
+// whole block (lane l: token l % 16, chunk l / 16) and a value transpose read
+// 512 contiguous bytes, so neither meets a bank conflict; one gather
+// instruction fills one block.
+__device__ __forceinline__ int tile_off(int t, int c) {
+  return (((c >> 2) << 1) + (t >> 4)) * 1024 + (((t & 15) + 16 * (c & 3)) << 4);
 }
-__device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ swz_key(t)) << 4); }
 
 template <bool FP8, bool OFF32>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
@@ -130,10 +134,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
   uint8_t* s_conv = s_main + kStages * kRingB;
 
-  const int row = blockIdx.x;
-  const int part = blockIdx.y / splits;
-  const int split = blockIdx.y % splits;
-  const int hg = blockIdx.z;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin in launch
+  // order, so the G = gridDim.y * gridDim.z workgroups of a row (its parts,
+  // splits and head groups, which all read the row's q) are given launch
+  // indices 8 apart inside one run of 8*G: same XCD, same dispatch round
+  int row, yz;
+  {
+    const int G = gridDim.y * gridDim.z;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int b = L / (8 * G), w = L % (8 * G);
+    const int nr = rows - 8 * b < 8 ? rows - 8 * b : 8;   // rows in this run
+    row = 8 * b + w % nr;
+    yz = w / nr;
+  }
+  const int part = (yz % gridDim.y) / splits;
+  const int split = (yz % gridDim.y) % splits;
+  const int hg = yz / gridDim.y;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int head = h0 + n16;
   const bool wave_on = h0 < heads;
   const bool head_on = head < heads;
-  const int out_part = blockIdx.y;
+  const int out_part = yz % gridDim.y;
 
   // ---- this split's slice of the part's token list --------------------------
   int cnt = counts ? counts[(int64_t)part * rows + row] : k;
@@ -185,21 +201,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   bar();   // slot list and flag ready (q may still be in flight)
 
   // ---- lane-invariant LDS byte offsets inside a bf16 tile -------------------
-  // scores: k-step kk reads token row tb + n16 (tb = 0, 16), logical chunk
-  // 4kk + g4; the key of rows n16 and 16 + n16 is the same and only touches
-  // the low 3 chunk bits, so the offset is qk_off[kk % 2] + 128 * (kk / 2)
-  int qk_off[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) qk_off[p] = chunk_off(n16, 4 * p + g4);
+  // scores: k-step kk, token block b reads block 2*kk + b at lane * 16.
   // values (transpose reads): in 16-lane group g4, source lane s = n16 reads
-  // token row 4*g4 + s/4 (+16 for the second read) at features 16*fb + 4*(s%4);
-  // logical chunk 2fb + (s%4)/2, so the offset is pv_off[fb % 4] + 128*(fb/4)
-  int pv_off[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 4 * g4 + (n16 >> 2);
-    pv_off[p] = chunk_off(r, 2 * p + ((n16 & 3) >> 1)) + 8 * (n16 & 1);
-  }
+  // token 16*rd + 4*g4 + s/4 at features 16*fb + 4*(s%4): logical chunk
+  // 2fb + (s%4)/2, half s%2, so the offset is pv_base + 2048*(fb/2) +
+  // 512*(fb%2) + 1024*rd
+  const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
 
   // ---- DMA issue of tile tt into its ring stage -------------------------------
   // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
@@ -216,15 +223,10 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       sv[jj] = 0;
       offv[jj] = 0;
       if (ins < kDmaTotal) {
-        const int p = ins * kWave + lane;
-        int t;
-        if constexpr (FP8) {
-          t = p / (kRowB8 / 16);
-          offv[jj] = (p % (kRowB8 / 16)) * 16;
-        } else {
-          t = p / kRowChunks;
-          offv[jj] = ((p % kRowChunks) ^ swz_key(t)) * 16;
-        }
+        // instruction ins fills block ins: tokens 16*(ins%2) + lane%16, 16-byte
+        // chunks 4*(ins/2) + lane/16 (bf16: 8 features; raw fp8: 16 features)
+        const int t = 16 * (ins & 1) + (lane & 15);
+        offv[jj] = (4 * (ins >> 1) + (lane >> 4)) * 16;
         const int ti = tbase + t < n_tok ? tbase + t : 0;
         sv[jj] = s_slot[ti];
       }
@@ -259,9 +261,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kQSteps; ++kk) {
-      const uint8_t* a = tile + qk_off[kk & 1] + 128 * (kk >> 1);
+      const uint8_t* a = tile + 2048 * kk + 16 * lane;
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 16 * kRowB);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 1024);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
     }
@@ -299,9 +301,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     // O^T += V^T P^T, 16 output features per block: ds_read_b64_tr_b16 gives
     // lane (g4, n16) element e = V[token 4*g4 + e (+16)][16*fb + n16]
     auto vfrag = [&](int fb) {
-      const uint8_t* b = tile + pv_off[fb & 3] + 128 * (fb >> 2);
+      const uint8_t* b = tile + pv_base + 2048 * (fb >> 1) + 512 * (fb & 1);
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b));
-      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 16 * kRowB));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 1024));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     bf16x8_t va = vfrag(0);
@@ -315,14 +317,18 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     }
   };
 
-  // fp8: widen raw tile tt into the swizzled bf16 layout of s_conv
+  // fp8: widen raw tile tt into the bf16 tile layout of s_conv.  The raw tile
+  // holds 18 blocks of 16 tokens x 4 chunks of 16 codes in gather order, so a
+  // thread reads one contiguous 16-byte slot and its two bf16 chunks land in
+  // slots that consecutive threads fill contiguously.
   auto widen = [&](int tt) {
     if constexpr (FP8) {
       const uint8_t* raw8 = s_ring[tt % kStages];
-      for (int c = tid; c < kTileB8 / 16; c += kAttnThreads) {
-        const int tr = c / (kRowB8 / 16);
-        const int c8 = c % (kRowB8 / 16);            // features 16*c8 .. +16
-        const uint4 rw = *reinterpret_cast<const uint4*>(raw8 + c * 16);
+      for (int d = tid; d < kTileB8 / 16; d += kAttnThreads) {
+        const int blk = d >> 6, l = d & 63;
+        const int tr = 16 * (blk & 1) + (l & 15);
+        const int rc = 4 * (blk >> 1) + (l >> 4);    // codes 16*rc .. +16
+        const uint4 rw = *reinterpret_cast<const uint4*>(raw8 + d * 16);
         const uint32_t w[4] = {rw.x, rw.y, rw.z, rw.w};
         uint32_t h[8];
 #pragma unroll
@@ -332,9 +338,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
           h[2 * q4] = __builtin_bit_cast(uint32_t, lo);
           h[2 * q4 + 1] = __builtin_bit_cast(uint32_t, hi);
         }
-        *reinterpret_cast<uint4*>(s_conv + chunk_off(tr, 2 * c8)) =
+        *reinterpret_cast<uint4*>(s_conv + tile_off(tr, 2 * rc)) =
             make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(s_conv + chunk_off(tr, 2 * c8 + 1)) =
+        *reinterpret_cast<uint4*>(s_conv + tile_off(tr, 2 * rc + 1)) =
             make_uint4(h[4], h[5], h[6], h[7]);
       }
     }
