@@ -161,7 +161,36 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const bool head_on = head < heads;
   const int out_part = yz % gridDim.y;
 
-  // ---- this split's slice of the part's token list --------------------------
+  // ---- startup loads: slot list, q, count ------------------------------------
+  // q fragments (B operand of S^T = K Q^T): head `head`, features 32*kk + 8*g4
+  // .. +8.  heads is a multiple of 16, so a wave's heads are all present or
+  // all absent; an absent wave loads head 0 (in bounds) and never uses it.
+  // Two load orders, chosen per cache type by measurement (the tile loop is
+  // the same code in both):
+  //  - bf16: the part's slot list (with one split it starts at position 0)
+  //    is requested together with the count instead of after it, all of a
+  //    thread's loads in flight at once, then q;
+  //  - fp8: count, then the list, then q, whose fragments are zeroed for
+  //    absent heads (the bf16 order measured ~7% slower here).
+  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
+  const uint16_t* qp = q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 8 * g4;
+  constexpr int kSlotLd = kMaxSel / kAttnThreads;
+  int sl[kSlotLd];
+  bf16x8_t qf[kQSteps];
+  if constexpr (!FP8) {
+    if (splits == 1) {
+#pragma unroll
+      for (int j = 0; j < kSlotLd; ++j) {
+        const int i = tid + j * kAttnThreads;
+        sl[j] = i < k ? my_slots[i] : -1;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kQSteps; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
+  }
+
+  // this split's slice of the part's token list
   int cnt = counts ? counts[(int64_t)part * rows + row] : k;
   cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
   if (num_slots <= 0) cnt = 0;
@@ -171,20 +200,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int n_tok = t_hi - t_lo;
   const int ntiles = (n_tok + kTile - 1) / kTile;
 
-  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
-  for (int i = tid; i < n_tok; i += kAttnThreads) {
-    const int s = my_slots[t_lo + i];
-    s_slot[i] = (s < 0 || (int64_t)s >= num_slots) ? -1 : s;
+  if (!FP8 && splits == 1) {
+#pragma unroll
+    for (int j = 0; j < kSlotLd; ++j) {
+      const int i = tid + j * kAttnThreads;
+      if (i < k) s_slot[i] = (sl[j] < 0 || (int64_t)sl[j] >= num_slots) ? -1 : sl[j];
+    }
+  } else {
+    for (int i = tid; i < n_tok; i += kAttnThreads) {
+      const int s = my_slots[t_lo + i];
+      s_slot[i] = (s < 0 || (int64_t)s >= num_slots) ? -1 : s;
+    }
   }
 
   const float kv_scale = FP8 ? cache_scale[0] : 1.0f;
   const float qk_scale = sm_scale * kv_scale * kLog2e;
-
-  // q fragments (B operand of S^T = K Q^T): head `head`, features
-  // 32*kk + 8*g4 .. +8 (in flight while the first tiles are requested)
-  bf16x8_t qf[kQSteps];
-  {
-    const uint16_t* qp = q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 8 * g4;
+  if constexpr (FP8) {
 #pragma unroll
     for (int kk = 0; kk < kQSteps; ++kk) {
       u16x8_t v = *reinterpret_cast<const u16x8_t*>(qp + 32 * kk);
