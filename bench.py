@@ -39,6 +39,8 @@ def parse():
                    choices=["decode", "tiny", "long", "prefill", "fp8"])
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="merge_candidates and convert_index as two launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (3 times), the reference "
@@ -71,11 +73,14 @@ def attention_traffic(c, counts_total):
     return bytes_, flops
 
 
-def topk_traffic(c, n_valid_logits):
-    """Algorithmic bytes of topk_select + merge_candidates for one step."""
+def topk_traffic(c, n_valid_logits, fused=True):
+    """Algorithmic bytes of topk_select and of the merge launch for one step
+    (merge_convert also writes the slot lists and counts)."""
     R, S, k = c.rows, c.S, c.k
     topk = n_valid_logits * 4 + R * S * k * 8         # logits read, candidates written
     merge = R * S * k * 8 + R * k * 4                 # candidates read, ids written
+    if fused:
+        merge += S * R * k * 4 + S * R * 4            # slots and counts written
     return topk, merge
 
 
@@ -161,8 +166,12 @@ def main():
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    names = ["fused_rmsnorm_rope", "topk_select", "merge_candidates", "convert_index",
-             "sparse_mla_decode", "lse_combine"]
+    if a.unfused:
+        names = ["fused_rmsnorm_rope", "topk_select", "merge_candidates", "convert_index",
+                 "sparse_mla_decode", "lse_combine"]
+    else:
+        names = ["fused_rmsnorm_rope", "topk_select", "merge_convert", "sparse_mla_decode",
+                 "lse_combine"]
 
     def step(i, att_ev=None, all_ev=None):
         """One pass of the whole path.  att_ev: events around the attention
@@ -170,22 +179,26 @@ def main():
         (the per-kernel breakdown pass, outside the timed region)."""
         j = i % a.sets
         rec = (lambda n: all_ev[n].record(stream)) if all_ev is not None else (lambda n: None)
-        rec(0)
+        n = 0
+        rec(n)
         if path.prologue is not None:
             path.run_prologue()
-        rec(1)
+        n += 1; rec(n)
         path.run_topk(logits=logits_sets[j])
-        rec(2)
-        path.run_merge()
-        rec(3)
-        path.run_convert()
-        rec(4)
+        n += 1; rec(n)
+        if a.unfused:
+            path.run_merge()
+            n += 1; rec(n)
+            path.run_convert()
+        else:
+            path.run_merge_convert()
+        n += 1; rec(n)
         if att_ev is not None: att_ev[0].record(stream)
         path.run_attention(q=q_sets[j])
         if att_ev is not None: att_ev[1].record(stream)
-        rec(5)
+        n += 1; rec(n)
         path.run_combine()
-        rec(6)
+        n += 1; rec(n)
 
     for i in range(a.warmup):
         step(i)
@@ -206,7 +219,8 @@ def main():
 
     # per-kernel breakdown: a separate pass with events between all launches
     n_brk = min(a.steps, 50)
-    brk = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_brk)]
+    brk = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(n_brk)]
     for i in range(n_brk):
         step(i, all_ev=brk[i])
     torch.cuda.synchronize()
@@ -221,7 +235,7 @@ def main():
     for i in range(c.rows):
         n_valid += int(c.row_ends[i]) - int(c.row_starts[i])
     att_bytes, att_flops = attention_traffic(c, counts_total)
-    tk_bytes, mg_bytes = topk_traffic(c, n_valid)
+    tk_bytes, mg_bytes = topk_traffic(c, n_valid, fused=not a.unfused)
     t_att = att_us * 1e-6
     att_gbs = att_bytes / t_att / 1e9
     att_tflops = att_flops / t_att / 1e12
@@ -238,8 +252,13 @@ def main():
     roof["algorithmic_flops"] = att_flops
     roof["mfma_tflops"] = round(att_tflops, 1)
 
-    t_topk = (kern_us["topk_select"] + kern_us["merge_candidates"]) * 1e-6
-    t_dec = (kern_us["convert_index"] + kern_us["sparse_mla_decode"] + kern_us["lse_combine"]) * 1e-6
+    # the metric's halves: top-K side = selection + merge (the fused launch
+    # counted whole), decode side = conversion (when separate) + attention +
+    # combine
+    merge_key = "merge_candidates" if a.unfused else "merge_convert"
+    t_topk = (kern_us["topk_select"] + kern_us[merge_key]) * 1e-6
+    t_dec = (kern_us.get("convert_index", 0.0) + kern_us["sparse_mla_decode"] +
+             kern_us["lse_combine"]) * 1e-6
     value = c.rows / (ms_per_step * 1e-3)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

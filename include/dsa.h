@@ -11,6 +11,7 @@
  *   dsa_fused_rmsnorm_rope (fp8 workload) -> dsa_topk_select (all shards)
  *   -> dsa_merge_candidates -> dsa_convert_index -> dsa_sparse_mla_decode
  *   -> dsa_lse_combine.
+ * dsa_merge_convert runs the merge and the conversion as one launch.
  * All shards of one job live on one GPU as slices of one buffer.
  *
  * Conventions shared by every entry point
@@ -146,6 +147,31 @@ int dsa_merge_candidates(const float* cand, int32_t rows, int32_t n_cand,
 int dsa_convert_index(const int32_t* ids, int32_t rows, int32_t k,
                       const int32_t* row_req, int32_t num_reqs,
                       const int32_t* block_table, int64_t bt_ld,
+                      int64_t bt_shard_stride, int32_t block_size,
+                      int32_t num_shards, int32_t interleave,
+                      int32_t shard_first, int32_t shard_count, int32_t* slots,
+                      int32_t* counts, hipStream_t stream);
+
+/*
+ * dsa_merge_convert — dsa_merge_candidates followed by dsa_convert_index of
+ * the merged ids, in one launch.
+ *
+ * Source: [A] 实现拆解 items 1 and 4 (the global merge of the gathered
+ * candidates, then each rank's conversion of the merged ids to its compacted
+ * local cache slots).  Every output equals what the two calls produce in
+ * sequence with the same arguments; the merged ids stay on chip in between.
+ *
+ * cand, n_cand, k, id_bound  as for dsa_merge_candidates.
+ * ids          [rows][k] int32 output as for dsa_merge_candidates (NULL: not
+ *              written).
+ * row_req, num_reqs, block_table, bt_ld, bt_shard_stride, block_size,
+ * num_shards, interleave, shard_first, shard_count, slots, counts  as for
+ *              dsa_convert_index.
+ * Errors: the union of both calls' checks.
+ */
+int dsa_merge_convert(const float* cand, int32_t rows, int32_t n_cand, int32_t k,
+                      int32_t id_bound, int32_t* ids, const int32_t* row_req,
+                      int32_t num_reqs, const int32_t* block_table, int64_t bt_ld,
                       int64_t bt_shard_stride, int32_t block_size,
                       int32_t num_shards, int32_t interleave,
                       int32_t shard_first, int32_t shard_count, int32_t* slots,

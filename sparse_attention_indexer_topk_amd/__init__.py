@@ -39,6 +39,8 @@ SIGNATURES = {
     "dsa_merge_candidates": [_P, _I32, _I32, _I32, _I32, _P, _P],
     "dsa_convert_index": [_P, _I32, _I32, _P, _I32, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32,
                           _P, _P, _P],
+    "dsa_merge_convert": [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _I64, _I64, _I32, _I32,
+                          _I32, _I32, _I32, _P, _P, _P],
     "dsa_sparse_mla_decode": [_P, _I32, _I32, _P, _I32, _P, _I64, _P, _P, _I32, _I32, _I32, _F32,
                               _P, _P, _P],
     "dsa_lse_combine": [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
@@ -157,6 +159,42 @@ def merge_candidates(cand: torch.Tensor, k: int, *, id_bound: int,
     return ids
 
 
+def merge_convert(cand: torch.Tensor, k: int, block_table: torch.Tensor, *, id_bound: int,
+                  block_size: int, num_shards: int, interleave: int,
+                  row_req: Optional[torch.Tensor] = None, shard_first: int = 0,
+                  ids: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None,
+                  counts: Optional[torch.Tensor] = None, want_ids: bool = True, stream=None):
+    """merge_candidates then convert_index in one launch.
+
+    cand [rows][n_cand][2] fp32 -> (ids [rows][k] or None, slots
+    [shard_count][rows][k], counts [shard_count][rows]).
+    """
+    _need(cand, "cand", torch.float32)
+    _need(block_table, "block_table", torch.int32)
+    if not cand.is_contiguous():
+        raise RuntimeError("cand must be contiguous")
+    rows, n_cand, _ = cand.shape
+    count, num_reqs, _ = block_table.shape
+    if row_req is not None:
+        _need(row_req, "row_req", torch.int32)
+    if ids is None and want_ids:
+        ids = torch.empty((rows, k), dtype=torch.int32, device=cand.device)
+    if ids is not None:
+        _need(ids, "ids", torch.int32)
+    if slots is None:
+        slots = torch.empty((count, rows, k), dtype=torch.int32, device=cand.device)
+    if counts is None:
+        counts = torch.empty((count, rows), dtype=torch.int32, device=cand.device)
+    _need(slots, "slots", torch.int32)
+    _need(counts, "counts", torch.int32)
+    _check(lib().dsa_merge_convert(
+        _ptr(cand), rows, n_cand, k, id_bound, _ptr(ids), _ptr(row_req), num_reqs,
+        _ptr(block_table), block_table.stride(1),
+        block_table.stride(0) if count > 1 else num_reqs * block_table.stride(1), block_size,
+        num_shards, interleave, shard_first, count, _ptr(slots), _ptr(counts), _stream(stream)))
+    return ids, slots, counts
+
+
 def convert_index(ids: torch.Tensor, block_table: torch.Tensor, *, block_size: int,
                   num_shards: int, interleave: int, row_req: Optional[torch.Tensor] = None,
                   shard_first: int = 0, slots: Optional[torch.Tensor] = None,
@@ -272,4 +310,4 @@ def fused_rmsnorm_rope(kv_c: torch.Tensor, k_pe: torch.Tensor, rms_w: torch.Tens
 
 
 __all__ = ["lib", "version", "DSAError", "topk_select", "merge_candidates", "convert_index",
-           "sparse_mla_decode", "lse_combine", "fused_rmsnorm_rope", "LIB_PATH", "SIGNATURES"]
+           "merge_convert", "sparse_mla_decode", "lse_combine", "fused_rmsnorm_rope", "LIB_PATH", "SIGNATURES"]

@@ -114,6 +114,36 @@ int dsa_convert_index(const int32_t* ids, int32_t rows, int32_t k, const int32_t
   return launched(fn);
 }
 
+int dsa_merge_convert(const float* cand, int32_t rows, int32_t n_cand, int32_t k,
+                      int32_t id_bound, int32_t* ids, const int32_t* row_req, int32_t num_reqs,
+                      const int32_t* block_table, int64_t bt_ld, int64_t bt_shard_stride,
+                      int32_t block_size, int32_t num_shards, int32_t interleave,
+                      int32_t shard_first, int32_t shard_count, int32_t* slots,
+                      int32_t* counts, hipStream_t stream) {
+  const char* fn = "dsa_merge_convert";
+  if (!cand || !block_table || !slots) return fail(DSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "%s: rows=%d < 0", fn, rows);
+  if (!k_ok(k)) return fail(DSA_ERR_UNSUPPORTED_K, "%s: k=%d not in {512, 1024, 2048}", fn, k);
+  if (n_cand < 1 || n_cand > DSA_MAX_SHARDS * k)
+    return fail(DSA_ERR_INVALID_ARG, "%s: n_cand=%d outside [1, 16*k]", fn, n_cand);
+  if (id_bound < 1 || id_bound > DSA_MAX_ID)
+    return fail(DSA_ERR_INVALID_ARG, "%s: id_bound=%d outside [1, 2^24]", fn, id_bound);
+  if (int rc = check_shards(fn, num_shards, interleave, shard_first, shard_count)) return rc;
+  if (num_reqs < 1) return fail(DSA_ERR_INVALID_ARG, "%s: num_reqs=%d < 1", fn, num_reqs);
+  if (bt_ld < 1) return fail(DSA_ERR_INVALID_ARG, "%s: bt_ld=%lld < 1", fn, (long long)bt_ld);
+  if (bt_shard_stride < 0 || (shard_count > 1 && bt_shard_stride < (int64_t)num_reqs * bt_ld))
+    return fail(DSA_ERR_INVALID_ARG, "%s: bt_shard_stride=%lld overlaps slices", fn,
+                (long long)bt_shard_stride);
+  if (block_size < 1) return fail(DSA_ERR_INVALID_ARG, "%s: block_size=%d < 1", fn, block_size);
+  if (!aligned(cand, 8) || !aligned(ids, 4))
+    return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (rows == 0) return DSA_OK;
+  dsa::launch_merge_convert(cand, rows, n_cand, k, id_bound, ids, row_req, num_reqs, block_table,
+                            bt_ld, bt_shard_stride, block_size, num_shards, interleave,
+                            shard_first, shard_count, slots, counts, stream);
+  return launched(fn);
+}
+
 int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void* cache,
                           int32_t cache_dtype, const float* cache_scale, int64_t num_slots,
                           const int32_t* slots, const int32_t* counts, int32_t k,

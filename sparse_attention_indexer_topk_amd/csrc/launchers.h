@@ -13,6 +13,11 @@ int launch_topk_select(const float* logits, int64_t ld, int64_t shard_stride, in
 int launch_merge_candidates(const float* cand, int rows, int n_cand, int k, int id_bound,
                             int* ids, hipStream_t stream);
 
+int launch_merge_convert(const float* cand, int rows, int n_cand, int k, int id_bound, int* ids,
+                         const int* row_req, int num_reqs, const int* block_table, int64_t bt_ld,
+                         int64_t bt_stride, int bs, int S, int I, int first, int count,
+                         int* slots, int* counts, hipStream_t stream);
+
 int launch_convert_index(const int* ids, int rows, int k, const int* row_req, int num_reqs,
                          const int* block_table, int64_t bt_ld, int64_t bt_stride, int bs,
                          int S, int I, int first, int count, int* slots, int* counts,

@@ -22,6 +22,17 @@
 //     2^18 ids; larger ranges are swept piecewise); each thread owns a run of
 //     bitmap words and a popcount scan gives each set bit its output slot;
 //     the ids are staged in LDS and leave in one coalesced write, -1 after.
+//
+// merge_convert_kernel continues in the same workgroup with the index
+// conversion (PR #46076 report, 实现拆解 item 4; the same result as
+// convert_index on the merged ids): the merged ids are already in LDS in
+// ascending order, so the per-shard compaction needs neither a second launch
+// nor a reload of the ids.  The merge of a row is latency-bound and occupies
+// one CU, so when rows alone leave CUs idle each (row, shard group) gets its
+// own workgroup, up to one per CU: it repeats the row's merge (its
+// candidates come from L2: the row's workgroups are launched on one XCD) and
+// converts only its group's shards; the conversion's stores are then spread
+// over more CUs.
 #include "launchers.h"
 #include "select_common.h"
 
@@ -41,7 +52,7 @@ struct MergeSmem {
   int stage[kMergeMaxK];
   uint32_t list[kMergeListCap];
   float red[2 * (kMergeThreads / kWave)];
-  uint32_t scan[kMergeThreads / kWave];
+  uint32_t scan[2][kMergeThreads / kWave];   // two, for back-to-back scans
   uint32_t res[4];
   uint32_t cnt;
   uint32_t nvalid;
@@ -53,10 +64,12 @@ __device__ __forceinline__ uint32_t key_to_bits(uint32_t key) {
   return (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
 }
 
+// Returns the number of ids kept; they are left in sm.stage in ascending
+// order (every thread has passed the barrier after they were written).
 template <int E, bool RESIDENT>
-__device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict__ src,
-                                          int n_cand, int k, int id_bound, bool vec,
-                                          int* __restrict__ out) {
+__device__ __forceinline__ int merge_row(MergeSmem& sm, const float* __restrict__ src,
+                                         int n_cand, int k, int id_bound, bool vec,
+                                         int* __restrict__ out) {
   constexpr int NT = kMergeThreads;
   constexpr int kChunk = NT * E;
   const int tid = threadIdx.x;
@@ -248,7 +261,7 @@ __device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict
       cnt += __popc(words[q]);
     }
     uint32_t total;
-    uint32_t pos = written + block_scan_excl<NT>(cnt, sm.scan, total);
+    uint32_t pos = written + block_scan_excl<NT>(cnt, sm.scan[0], total);
 #pragma unroll
     for (int q = 0; q < kIdWordsPerThread; ++q) {
       uint32_t w = words[q];
@@ -263,7 +276,74 @@ __device__ __forceinline__ void merge_row(MergeSmem& sm, const float* __restrict
   }
   __syncthreads();
   const int n_out = (int)(written < (uint32_t)k ? written : (uint32_t)k);
-  for (int i = tid; i < k; i += NT) out[i] = i < n_out ? sm.stage[i] : -1;
+  if (out)
+    for (int i = tid; i < k; i += NT) out[i] = i < n_out ? sm.stage[i] : -1;
+  return n_out;
+}
+
+// ---- index conversion of the merged ids (merge_convert_kernel) -------------
+struct ConvertArgs {
+  const int* row_req;       // nullable: row i -> request i
+  int num_reqs;
+  const int* block_table;   // [count][num_reqs][bt_ld], slice j at + j * bt_stride
+  int64_t bt_ld, bt_stride;
+  int bs, S, I, first, count, rows;
+  int* slots;               // [count][rows][k]
+  int* counts;              // nullable, [count][rows]
+  int groups;               // workgroups per row, each converting `per` shards
+  int per;
+};
+
+// Thread t resolves merged positions [t*P, t*P + P): owner shard, local
+// position, block-table slot (all lookups in flight together).  Per shard,
+// a block exclusive scan of the per-thread counts places the slots in input
+// order; two shards share one scan as 16-bit fields (a row keeps at most 2048
+// ids, so no field carries into the next).
+__device__ __forceinline__ void convert_tail(MergeSmem& sm, int n_out, int k, int row,
+                                             int j_lo, int j_hi, const ConvertArgs& cv) {
+  constexpr int NT = kMergeThreads;
+  constexpr int P = kMergeMaxK / NT;
+  const int tid = threadIdx.x;
+  const int req = cv.row_req ? cv.row_req[row] : row;
+  const bool req_ok = req >= 0 && req < cv.num_reqs;
+  int jj[P], slot[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    jj[p] = -1;
+    slot[p] = 0;
+    const int i = tid * P + p;
+    if (req_ok && i < n_out) {
+      const int g = sm.stage[i];
+      const int j = owner_of(g, cv.S, cv.I) - cv.first;
+      if (j >= j_lo && j < j_hi) {
+        const int l = local_of(g, cv.S, cv.I);
+        const int c = l / cv.bs;
+        if ((int64_t)c < cv.bt_ld) {
+          jj[p] = j;
+          slot[p] = cv.block_table[(int64_t)j * cv.bt_stride + (int64_t)req * cv.bt_ld + c] *
+                        cv.bs + (l - c * cv.bs);
+        }
+      }
+    }
+  }
+  for (int j0 = j_lo; j0 < j_hi; j0 += 2) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) c += jj[p] == j0 ? 1u : (jj[p] == j0 + 1 ? 0x10000u : 0u);
+    uint32_t total;
+    const uint32_t pos = block_scan_excl<NT>(c, sm.scan[((j0 - j_lo) >> 1) & 1], total);
+    for (int h = 0; h < 2 && j0 + h < j_hi; ++h) {
+      const int j = j0 + h;
+      uint32_t ps = (pos >> (16 * h)) & 0xffffu;
+      const int tot = (int)((total >> (16 * h)) & 0xffffu);
+      int* dst = cv.slots + ((int64_t)j * cv.rows + row) * k;
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (jj[p] == j) dst[ps++] = slot[p];
+      for (int i = tot + tid; i < k; i += NT) dst[i] = -1;
+      if (tid == 0 && cv.counts) cv.counts[(int64_t)j * cv.rows + row] = tot;
+    }
+  }
 }
 
 template <int E>
@@ -278,6 +358,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_candidates_kernel(
     merge_row<E, true>(sm, src, n_cand, k, id_bound, vec != 0, out);
   else
     merge_row<E, false>(sm, src, n_cand, k, id_bound, vec != 0, out);
+}
+
+template <int E>
+__global__ __launch_bounds__(kMergeThreads) void merge_convert_kernel(
+    const float* __restrict__ cand, int n_cand, int k, int id_bound, int* __restrict__ ids,
+    int vec, ConvertArgs cv) {
+  __shared__ MergeSmem sm;
+  // XCD-aware order: launch index L -> (row, group) with the G groups of a
+  // row 8 launch indices apart inside a run of 8*G (same XCD, same round)
+  const int G = cv.groups;
+  const int L = blockIdx.x;
+  const int b = L / (8 * G), w = L % (8 * G);
+  const int nr = cv.rows - 8 * b < 8 ? cv.rows - 8 * b : 8;
+  const int row = 8 * b + w % nr;
+  const int grp = w / nr;
+  const int j_lo = grp * cv.per;
+  const int j_hi = j_lo + cv.per < cv.count ? j_lo + cv.per : cv.count;
+  const float* src = cand + (int64_t)row * n_cand * 2;
+  int* out = (ids && grp == 0) ? ids + (int64_t)row * k : nullptr;
+  const int n_out = n_cand <= kMergeThreads * E
+                        ? merge_row<E, true>(sm, src, n_cand, k, id_bound, vec != 0, out)
+                        : merge_row<E, false>(sm, src, n_cand, k, id_bound, vec != 0, out);
+  convert_tail(sm, n_out, k, row, j_lo, j_hi, cv);
+}
+
+int launch_merge_convert(const float* cand, int rows, int n_cand, int k, int id_bound, int* ids,
+                         const int* row_req, int num_reqs, const int* block_table, int64_t bt_ld,
+                         int64_t bt_stride, int bs, int S, int I, int first, int count,
+                         int* slots, int* counts, hipStream_t stream) {
+  const int vec = ((uintptr_t)cand % 16 == 0 && n_cand % 2 == 0) ? 1 : 0;
+  // as many shard groups per row as keep the launch within one workgroup
+  // per CU (a second merge on a CU costs more than the conversion it
+  // spreads); with 256 rows or more, one workgroup per row converts every
+  // shard
+  constexpr int kCUs = 256;
+  const int g0 = std::max(1, std::min(count, kCUs / std::max(rows, 1)));
+  const int per = (count + g0 - 1) / g0;
+  const int groups = (count + per - 1) / per;   // no empty group
+  const ConvertArgs cv{row_req, num_reqs, block_table, bt_ld, bt_stride, bs, S, I, first,
+                       count, rows, slots, counts, groups, per};
+  const dim3 grid((unsigned)((int64_t)rows * groups));
+  if (n_cand <= kMergeThreads * 8)
+    hipLaunchKernelGGL((merge_convert_kernel<8>), grid, dim3(kMergeThreads), 0, stream, cand,
+                       n_cand, k, id_bound, ids, vec, cv);
+  else
+    hipLaunchKernelGGL((merge_convert_kernel<16>), grid, dim3(kMergeThreads), 0, stream, cand,
+                       n_cand, k, id_bound, ids, vec, cv);
+  return 0;
 }
 
 int launch_merge_candidates(const float* cand, int rows, int n_cand, int k, int id_bound,

@@ -6,7 +6,7 @@ makes ([A]: PR #46076 report, 实现拆解 items 1-5; [C]: PR #52046 report,
 
   fused_rmsnorm_rope (optional: new K rows materialised and inserted)
   -> topk_select (all shards, one launch; writes the gathered candidates)
-  -> merge_candidates -> convert_index (all shards)
+  -> merge_candidates + convert_index (all shards; one launch, merge_convert)
   -> sparse_mla_decode (all shards, one launch) -> lse_combine.
 
 Only sequencing and buffer ownership live here; the arithmetic is in the HIP
@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-from . import (topk_select, merge_candidates, convert_index, sparse_mla_decode, lse_combine,
-               fused_rmsnorm_rope)
+from . import (topk_select, merge_candidates, convert_index, merge_convert, sparse_mla_decode,
+               lse_combine, fused_rmsnorm_rope)
 
 
 @dataclasses.dataclass
@@ -94,6 +94,12 @@ class DecodePath:
                       interleave=self.I, row_req=self.row_req, slots=self.slots,
                       counts=self.counts, stream=stream)
 
+    def run_merge_convert(self, stream=None):
+        merge_convert(self.cand, self.k, self.block_table, id_bound=self.ctx,
+                      block_size=self.block_size, num_shards=self.S, interleave=self.I,
+                      row_req=self.row_req, ids=self.ids, slots=self.slots, counts=self.counts,
+                      stream=stream)
+
     def run_attention(self, stream=None, q=None):
         sparse_mla_decode(self.q if q is None else q, self.cache, self.slots, self.counts,
                           sm_scale=self.sm_scale, splits=self.splits,
@@ -107,7 +113,6 @@ class DecodePath:
         if self.prologue is not None:
             self.run_prologue(stream)
         self.run_topk(stream, with_local_idx)
-        self.run_merge(stream)
-        self.run_convert(stream)
+        self.run_merge_convert(stream)
         self.run_attention(stream)
         self.run_combine(stream)

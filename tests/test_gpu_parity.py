@@ -99,6 +99,15 @@ def test_path_matches_oracle_every_stage(name):
     assert np.array_equal(path.slots.cpu().numpy(), oslots)
     assert np.array_equal(path.counts.cpu().numpy(), ocounts)
 
+    # the fused launch the bench times: the same three outputs
+    fids, fslots, fcounts = dsa.merge_convert(
+        path.cand, c.k, path.block_table, id_bound=c.ctx, block_size=64, num_shards=c.S,
+        interleave=c.I, row_req=path.row_req)
+    torch.cuda.synchronize()
+    assert np.array_equal(fids.cpu().numpy(), oids)
+    assert np.array_equal(fslots.cpu().numpy(), oslots)
+    assert np.array_equal(fcounts.cpu().numpy(), ocounts)
+
     opo, opl = oracle.sparse_mla_partial(c.q, cache_ref, c.cache_dtype, c.cache_scale, oslots,
                                          ocounts, c.sm_scale)
     oo, ol = oracle.lse_combine(opo, opl)
@@ -162,8 +171,7 @@ def test_full_size_workload_sampled_rows(name):
         rows_oracle = check_prologue(c, path)
     log(f"[full] workload {name}: running the step")
     path.run_topk()
-    path.run_merge()
-    path.run_convert()
+    path.run_merge_convert()          # the launch sequence the bench times
     path.run_attention()
     path.run_combine()
     torch.cuda.synchronize()

@@ -14,6 +14,10 @@ an id range needing several bitmap sweeps.
 
 Convert: rows whose request is outside the table.
 
+Merge + convert in one launch: shard sub-ranges, odd shard counts, k = 512,
+ties, padding, missing requests, a narrow table, with and without the ids
+output.
+
 Every selection result is compared element by element (bit for bit) with the
 oracle.
 
@@ -253,6 +257,53 @@ def test_convert_rows_outside_table():
     torch.cuda.synchronize()
     assert np.array_equal(gs.cpu().numpy(), es)
     assert np.array_equal(gc.cpu().numpy(), ec)
+
+
+# ---------------------------------------------------- merge + convert, fused --
+@pytest.mark.parametrize("k,S,I,first,count,narrow,R",
+                         [(2048, 16, 3, 0, 16, False, 5), (512, 5, 64, 1, 3, True, 5),
+                          (1024, 4, 1, 3, 1, False, 5), (512, 4, 2, 0, 4, True, 300),
+                          (512, 6, 1, 0, 6, False, 60)])
+def test_merge_convert_matches_oracle(k, S, I, first, count, narrow, R):
+    """merge_convert equals merge_candidates then convert_index: an odd number
+    of shards in the run (a lone field in the last paired scan), a shard
+    sub-range, k = 512 (threads past the merged ids idle), ties and padding
+    among the candidates, a row with no valid candidate, a row whose request
+    is outside the table, a table narrower than the ids (dropped ids), and
+    the ids output left out.  The launch splits a row's shards into groups,
+    one workgroup each, within one workgroup per CU: 300 rows convert every
+    shard in one workgroup (paired scans), 60 rows x 6 shards make three
+    groups of two, five rows one group per shard."""
+    B, bs, Rq = 60000, 64, 4
+    N = min(S * k, 16 * k)
+    cand = make_cand(R, N, B, 30 + k + S)
+    cand[1, :, 0] = np.round(cand[1, :, 0] * 8.0) / 8.0      # ties at the threshold
+    cand[2, N // 3:, 1] = -1.0                               # padding entries
+    cand[3, :, 1] = -1.0                                     # no valid candidate
+    W = (int(oracle.local_count(B, 0, S, I)) + bs - 1) // bs
+    if narrow:
+        W -= 3                                               # ids past the table drop
+    r = np.random.default_rng(31)
+    bt = r.permutation(count * Rq * W).astype(np.int32).reshape(count, Rq, W)
+    row_req = np.arange(R, dtype=np.int32) % Rq
+    row_req[-1] = 7                                          # the last row: no request
+    eids = oracle.merge_candidates(cand, k)
+    es, ec = oracle.convert_index(eids, row_req, bt, bs, S, I, first=first, count=count)
+    dcand = torch.from_numpy(cand).to(DEV)
+    dbt = torch.from_numpy(bt).to(DEV)
+    drq = torch.from_numpy(row_req).to(DEV)
+    log(f"merge_convert k={k} S={S} I={I} run [{first}, {first + count})")
+    for want_ids in (True, False):
+        gids, gs, gc = dsa.merge_convert(dcand, k, dbt, id_bound=B, block_size=bs, num_shards=S,
+                                         interleave=I, row_req=drq, shard_first=first,
+                                         want_ids=want_ids)
+        torch.cuda.synchronize()
+        if want_ids:
+            assert np.array_equal(gids.cpu().numpy(), eids)
+        else:
+            assert gids is None
+        assert np.array_equal(gs.cpu().numpy(), es)
+        assert np.array_equal(gc.cpu().numpy(), ec)
 
 
 # ------------------------------------------------------------ attention --
