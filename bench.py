@@ -39,6 +39,9 @@ def parse():
                    choices=["decode", "tiny", "long", "prefill", "fp8"])
     p.add_argument("--sets", type=int, default=4, help="rotating input sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--pcp", type=int, default=0,
+                   help="prologue in sequence-sharded form over this many ranks "
+                        "(materialise per rank, gather, insert)")
     p.add_argument("--unfused", action="store_true",
                    help="merge_candidates and convert_index as two launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -156,6 +159,11 @@ def main():
     t_gen = time.perf_counter()
     c = dsa_inputs.make(a.workload)
     arrays = dsa_inputs.device_arrays(c, device=dev)
+    if a.pcp:
+        if "prologue" not in arrays:
+            print("--pcp needs a workload with a prologue (fp8)", file=sys.stderr)
+            sys.exit(2)
+        arrays["pcp_ranks"] = a.pcp
     path = DecodePath(**arrays)
     logits_sets, q_sets = [path.logits], [path.q]
     for s in range(1, a.sets):
@@ -172,6 +180,8 @@ def main():
     else:
         names = ["fused_rmsnorm_rope", "topk_select", "merge_convert", "sparse_mla_decode",
                  "lse_combine"]
+    if a.pcp:   # per-rank materialise launches + one insert
+        names[0] = "prologue_pcp"
 
     def step(i, att_ev=None, all_ev=None):
         """One pass of the whole path.  att_ev: events around the attention
@@ -227,7 +237,7 @@ def main():
     kern_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in brk])) * 1e3
                for j, n in enumerate(names)}
     if path.prologue is None:
-        kern_us.pop("fused_rmsnorm_rope")
+        kern_us.pop(names[0])
 
     # algorithmic traffic of the last set's step (all sets have the same shape)
     counts_total = int(path.counts.sum().item())
@@ -267,7 +277,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": c.spec.name, "rows": c.rows, "ctx": c.ctx, "k": c.k,
                    "shards": c.S, "interleave": c.I, "heads": c.heads, "cache": c.cache_dtype,
-                   "input_sets": a.sets},
+                   "input_sets": a.sets, **({"pcp_ranks": a.pcp} if a.pcp else {})},
         "topk_rows_per_s": round(c.rows / t_topk, 1),
         "decode_tokens_per_s": round(c.rows / t_dec, 1),
         "sparse_mla_decode_us_timed": round(att_us, 2),

@@ -71,6 +71,7 @@ class Spec:
     fp8_scale: float = 2.0 ** -4
     q_pos_step: int = 1             # causal: row i ends at 1 + i*step
     q_len: int = 1                  # query tokens per request (multi-token decode)
+    pcp: int = 0                    # >0: prologue in sequence-sharded (PCP) form over pcp ranks
 
 
 CONFIGS = {
@@ -113,6 +114,12 @@ PARITY_CASES = {
     # block table; 2 shards, as in the pages' [4, 4, 5] localisation example
     "mtp_s": Spec("mtp_s", rows=9, ctx=9001, shards=2, interleave=1, k=512,
                   heads=16, seed=18, q_len=3),
+    # sequence-sharded (PCP) prefill chunk over a replicated fp8 cache: no
+    # context sharding; the new K rows are materialised by 3 ranks, gathered
+    # and inserted (materialise -> gather -> insert)
+    "pcp_s": Spec("pcp_s", rows=24, ctx=3000, shards=1, interleave=1, k=512,
+                  heads=16, seed=19, logits="causal", one_request=True,
+                  row_ends="causal", q_pos_step=113, cache="fp8", prologue=True, pcp=3),
 }
 
 
@@ -406,6 +413,8 @@ def device_arrays(case: Case, device="cuda", logits=None, q=None) -> dict:
         d["prologue"] = dict(kv_c=bf16(case.kv_c), k_pe=bf16(case.k_pe), rms_w=bf16(case.rms_w),
                              eps=float(case.rms_eps), cos_sin=dev(case.cos_sin),
                              positions=dev(case.positions), slot_mapping=dev(case.slot_mapping))
+        if sp.pcp:
+            d["pcp_ranks"] = sp.pcp
     return d
 
 

@@ -269,6 +269,31 @@ int dsa_fused_rmsnorm_rope(const void* kv_c, int64_t kv_c_ld, const void* k_pe,
                            const int64_t* slot_mapping, int64_t num_slots,
                            hipStream_t stream);
 
+/*
+ * dsa_cache_insert — write already materialised K rows into the latent cache.
+ *
+ * Source: [C] 关键源码片段 (the PCP branch of `_sparse_indexer_and_attn`):
+ * with queries sharded by sequence the MLA cache is replicated, so the new K
+ * rows every rank materialised are gathered (`maybe_gather_mla_latent_cache_
+ * inputs`) and then written into each replica (`do_kv_cache_update` with the
+ * cache dtype and k scale).  The values are written exactly as the insert of
+ * dsa_fused_rmsnorm_rope writes its materialised rows, so materialise +
+ * gather + insert equals the fused insert bit for bit.
+ *
+ * kv_c [T][kv_c_ld] bf16 (first 512), k_pe [T][k_pe_ld] bf16 (first 64):
+ *              the materialised rows.
+ * cache [num_slots][576] bf16 or fp8 e4m3 per cache_dtype; cache_scale device
+ *              fp32 scalar (fp8): entries are e4m3(value / scale),
+ *              nearest-even, saturating at 448.
+ * slot_mapping [T] int64 (entries < 0 or >= num_slots are skipped).
+ * Errors: INVALID_ARG (null pointers, T < 0, lds < widths, misaligned),
+ * UNSUPPORTED_DTYPE.
+ */
+int dsa_cache_insert(const void* kv_c, int64_t kv_c_ld, const void* k_pe,
+                     int64_t k_pe_ld, int32_t T, void* cache, int32_t cache_dtype,
+                     const float* cache_scale, const int64_t* slot_mapping,
+                     int64_t num_slots, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dsa_last_error(void);
 

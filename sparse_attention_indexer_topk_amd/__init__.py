@@ -46,6 +46,7 @@ SIGNATURES = {
     "dsa_lse_combine": [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
     "dsa_fused_rmsnorm_rope": [_P, _I64, _P, _I64, _I32, _P, _F32, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                _P, _I64, _P],
+    "dsa_cache_insert": [_P, _I64, _P, _I64, _I32, _P, _I32, _P, _P, _I64, _P],
     "dsa_last_error": [],
     "dsa_version": [],
 }
@@ -309,5 +310,21 @@ def fused_rmsnorm_rope(kv_c: torch.Tensor, k_pe: torch.Tensor, rms_w: torch.Tens
     return kv_c_out, k_pe_out
 
 
+def cache_insert(kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
+                 slot_mapping: torch.Tensor, *, cache_scale: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Write materialised K rows (kv_c [T][512], k_pe [T][64] bf16) into ``cache``
+    at ``slot_mapping`` (bf16, or fp8 e4m3 scaled by ``cache_scale``)."""
+    _bits16(kv_c, "kv_c")
+    _bits16(k_pe, "k_pe")
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    T = kv_c.shape[0]
+    cdt = DSA_FP8_E4M3 if cache.dtype in (torch.uint8, torch.float8_e4m3fn) else DSA_BF16
+    _check(lib().dsa_cache_insert(
+        _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), T, _ptr(cache), cdt,
+        _ptr(cache_scale), _ptr(slot_mapping), cache.numel() // 576, _stream(stream)))
+
+
 __all__ = ["lib", "version", "DSAError", "topk_select", "merge_candidates", "convert_index",
-           "merge_convert", "sparse_mla_decode", "lse_combine", "fused_rmsnorm_rope", "LIB_PATH", "SIGNATURES"]
+           "merge_convert", "sparse_mla_decode", "lse_combine", "fused_rmsnorm_rope",
+           "cache_insert", "LIB_PATH", "SIGNATURES"]

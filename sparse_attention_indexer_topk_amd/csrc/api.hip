@@ -232,4 +232,32 @@ int dsa_fused_rmsnorm_rope(const void* kv_c, int64_t kv_c_ld, const void* k_pe, 
   return launched(fn);
 }
 
+int dsa_cache_insert(const void* kv_c, int64_t kv_c_ld, const void* k_pe, int64_t k_pe_ld,
+                     int32_t T, void* cache, int32_t cache_dtype, const float* cache_scale,
+                     const int64_t* slot_mapping, int64_t num_slots, hipStream_t stream) {
+  const char* fn = "dsa_cache_insert";
+  if (T < 0) return fail(DSA_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
+  if (!kv_c || !k_pe || !cache || !slot_mapping)
+    return fail(DSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (kv_c_ld < DSA_VALUE_DIM || kv_c_ld % 8 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: kv_c_ld=%lld must be >= 512 and a multiple of 8", fn,
+                (long long)kv_c_ld);
+  if (k_pe_ld < DSA_ROPE_DIM || k_pe_ld % 2 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: k_pe_ld=%lld must be >= 64 and even", fn,
+                (long long)k_pe_ld);
+  int kind;
+  if (cache_dtype == DSA_BF16) kind = 1;
+  else if (cache_dtype == DSA_FP8_E4M3) kind = 2;
+  else return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: cache dtype %d is not bf16 or fp8", fn,
+                   cache_dtype);
+  if (kind == 2 && !cache_scale) return fail(DSA_ERR_INVALID_ARG, "%s: fp8 cache needs cache_scale", fn);
+  if (num_slots < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_slots < 0", fn);
+  if (!aligned(kv_c, 16) || !aligned(k_pe, 4) || !aligned(cache, 16) || !aligned(slot_mapping, 8))
+    return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (T == 0) return DSA_OK;
+  dsa::launch_cache_insert(kv_c, kv_c_ld, k_pe, k_pe_ld, T, cache, kind, cache_scale,
+                           slot_mapping, num_slots, stream);
+  return launched(fn);
+}
+
 }  // extern "C"

@@ -12,6 +12,12 @@
 // How: one wave per token; each lane owns 8 contiguous kv_c elements (16-byte
 // load) and lanes 0..31 one rope pair; the sum of squares is a wave
 // butterfly; math in fp32; stores are 16 bytes (bf16) / 8 bytes (fp8).
+//
+// cache_insert_kernel writes already materialised rows (the K rows that the
+// sequence-sharded (PCP) path gathers from every rank before the update of
+// its replicated cache: PR #52046 report, 关键源码片段, `do_kv_cache_update`
+// after `maybe_gather_mla_latent_cache_inputs`) through the same insert
+// code, so materialise + gather + insert equals the fused insert bit for bit.
 #include "launchers.h"
 
 namespace dsa {
@@ -22,6 +28,36 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
+}
+
+// Writes one cache entry [y | r] (8 kv_c values per lane; lanes 0..31 one
+// rope pair): bf16 as is, fp8 as e4m3(value / scale).
+template <int CACHE>
+__device__ __forceinline__ void insert_row(int lane, const uint16_t (&y)[8], uint16_t r1b,
+                                           uint16_t r2b, void* __restrict__ cache,
+                                           const float* __restrict__ cache_scale, int64_t slot) {
+  if constexpr (CACHE == 1) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + slot * kLatent;
+    *reinterpret_cast<uint4*>(dst + 8 * lane) =
+        make_uint4(y[0] | ((uint32_t)y[1] << 16), y[2] | ((uint32_t)y[3] << 16),
+                   y[4] | ((uint32_t)y[5] << 16), y[6] | ((uint32_t)y[7] << 16));
+    if (lane < kRope / 2)
+      *reinterpret_cast<uint32_t*>(dst + kValue + 2 * lane) = (uint32_t)r1b | ((uint32_t)r2b << 16);
+  } else {
+    const float sc = cache_scale[0];
+    uint8_t* dst = reinterpret_cast<uint8_t*>(cache) + slot * kLatent;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(bf16_to_f32(y[e]) / sc) << (8 * e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(bf16_to_f32(y[4 + e]) / sc) << (8 * e);
+    *reinterpret_cast<uint2*>(dst + 8 * lane) = make_uint2(lo, hi);
+    if (lane < kRope / 2) {
+      const uint32_t c1 = f32_to_e4m3(bf16_to_f32(r1b) / sc);
+      const uint32_t c2 = f32_to_e4m3(bf16_to_f32(r2b) / sc);
+      *reinterpret_cast<uint16_t*>(dst + kValue + 2 * lane) = (uint16_t)(c1 | (c2 << 8));
+    }
+  }
 }
 
 // CACHE: 0 = no insert, 1 = bf16 cache, 2 = fp8 e4m3 cache
@@ -81,26 +117,49 @@ __global__ __launch_bounds__(kNormThreads) void fused_rmsnorm_rope_kernel(
   if constexpr (CACHE != 0) {
     const int64_t slot = slot_mapping[t];
     if (slot < 0 || slot >= num_slots) return;
-    if constexpr (CACHE == 1) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + slot * kLatent;
-      *reinterpret_cast<uint4*>(dst + 8 * lane) = yv;
-      if (lane < kRope / 2) *reinterpret_cast<uint32_t*>(dst + kValue + 2 * lane) = rv;
-    } else {
-      const float sc = cache_scale[0];
-      uint8_t* dst = reinterpret_cast<uint8_t*>(cache) + slot * kLatent;
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(bf16_to_f32(y[e]) / sc) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(bf16_to_f32(y[4 + e]) / sc) << (8 * e);
-      *reinterpret_cast<uint2*>(dst + 8 * lane) = make_uint2(lo, hi);
-      if (lane < kRope / 2) {
-        const uint32_t c1 = f32_to_e4m3(bf16_to_f32(r1b) / sc);
-        const uint32_t c2 = f32_to_e4m3(bf16_to_f32(r2b) / sc);
-        *reinterpret_cast<uint16_t*>(dst + kValue + 2 * lane) = (uint16_t)(c1 | (c2 << 8));
-      }
-    }
+    insert_row<CACHE>(lane, y, r1b, r2b, cache, cache_scale, slot);
   }
+}
+
+// CACHE: 1 = bf16 cache, 2 = fp8 e4m3 cache
+template <int CACHE>
+__global__ __launch_bounds__(kNormThreads) void cache_insert_kernel(
+    const uint16_t* __restrict__ kv_c, int64_t kv_ld, const uint16_t* __restrict__ k_pe,
+    int64_t pe_ld, int T, void* __restrict__ cache, const float* __restrict__ cache_scale,
+    const int64_t* __restrict__ slot_mapping, int64_t num_slots) {
+  const int t = blockIdx.x * (kNormThreads / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int lane = lane_id();
+  const uint4 xv = *reinterpret_cast<const uint4*>(kv_c + (int64_t)t * kv_ld + 8 * lane);
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  uint16_t y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (uint16_t)(xw[e >> 1] >> (16 * (e & 1)));
+  uint16_t r1b = 0, r2b = 0;
+  if (lane < kRope / 2) {
+    const uint32_t pr = *reinterpret_cast<const uint32_t*>(k_pe + (int64_t)t * pe_ld + 2 * lane);
+    r1b = (uint16_t)(pr & 0xffffu);
+    r2b = (uint16_t)(pr >> 16);
+  }
+  insert_row<CACHE>(lane, y, r1b, r2b, cache, cache_scale, slot);
+}
+
+int launch_cache_insert(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld, int T,
+                        void* cache, int cache_kind, const float* cache_scale,
+                        const int64_t* slot_mapping, int64_t num_slots, hipStream_t stream) {
+  const int wpb = kNormThreads / kWave;
+  dim3 grid((T + wpb - 1) / wpb);
+  auto a0 = reinterpret_cast<const uint16_t*>(kv_c);
+  auto a1 = reinterpret_cast<const uint16_t*>(k_pe);
+  if (cache_kind == 1)
+    hipLaunchKernelGGL(cache_insert_kernel<1>, grid, dim3(kNormThreads), 0, stream, a0, kv_ld, a1,
+                       pe_ld, T, cache, cache_scale, slot_mapping, num_slots);
+  else
+    hipLaunchKernelGGL(cache_insert_kernel<2>, grid, dim3(kNormThreads), 0, stream, a0, kv_ld, a1,
+                       pe_ld, T, cache, cache_scale, slot_mapping, num_slots);
+  return 0;
 }
 
 int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld,

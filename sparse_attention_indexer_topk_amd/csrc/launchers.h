@@ -31,6 +31,10 @@ int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cac
 int launch_lse_combine(const void* part_out, const float* part_lse, int P, int rows, int heads,
                        int dim, void* out, float* lse_out, hipStream_t stream);
 
+int launch_cache_insert(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld, int T,
+                        void* cache, int cache_kind, const float* cache_scale,
+                        const int64_t* slot_mapping, int64_t num_slots, hipStream_t stream);
+
 int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld,
                               int T, const void* w, float eps, const float* cos_sin, int n_pos,
                               const int* positions, void* kv_out, void* pe_out, void* cache,

@@ -4,7 +4,9 @@ The step is the sequence of library calls the decode-context-parallel path
 makes ([A]: PR #46076 report, 实现拆解 items 1-5; [C]: PR #52046 report,
 关键源码片段), with every shard emulated as a slice of one buffer:
 
-  fused_rmsnorm_rope (optional: new K rows materialised and inserted)
+  fused_rmsnorm_rope (optional: new K rows materialised and inserted; in the
+  sequence-sharded (PCP) form each rank materialises its rows, the rows are
+  gathered and cache_insert writes them all)
   -> topk_select (all shards, one launch; writes the gathered candidates)
   -> merge_candidates + convert_index (all shards; one launch, merge_convert)
   -> sparse_mla_decode (all shards, one launch) -> lse_combine.
@@ -20,7 +22,7 @@ from typing import Optional
 import torch
 
 from . import (topk_select, merge_candidates, convert_index, merge_convert, sparse_mla_decode,
-               lse_combine, fused_rmsnorm_rope)
+               lse_combine, fused_rmsnorm_rope, cache_insert)
 
 
 @dataclasses.dataclass
@@ -42,7 +44,7 @@ class DecodePath:
                  interleave: int, q: torch.Tensor, cache: torch.Tensor,
                  cache_scale: Optional[torch.Tensor], block_table: torch.Tensor,
                  row_req: Optional[torch.Tensor], sm_scale: float, block_size: int = 64,
-                 prologue=None, splits: Optional[int] = None):
+                 prologue=None, splits: Optional[int] = None, pcp_ranks: int = 0):
         self.logits, self.row_starts, self.row_ends = logits, row_starts, row_ends
         self.ctx, self.k, self.S, self.I = ctx, k, num_shards, interleave
         self.q, self.cache, self.cache_scale = q, cache, cache_scale
@@ -51,6 +53,10 @@ class DecodePath:
         if isinstance(prologue, dict):
             prologue = Prologue(**prologue)
         self.prologue = prologue
+        # pcp_ranks > 0: the sequence-sharded (PCP) prologue -- each rank
+        # materialises its slice of the new K rows into the gathered buffer
+        # (the all-gather, in place), then every row is inserted
+        self.pcp_ranks = pcp_ranks
         dev = logits.device
         R, H = q.shape[0], q.shape[1]
         S = num_shards
@@ -75,10 +81,21 @@ class DecodePath:
     # -- steps ---------------------------------------------------------------
     def run_prologue(self, stream=None):
         p = self.prologue
-        fused_rmsnorm_rope(p.kv_c, p.k_pe, p.rms_w, p.eps, p.cos_sin, p.positions,
-                           kv_c_out=self.kv_c_out, k_pe_out=self.k_pe_out, cache=self.cache,
-                           cache_scale=self.cache_scale, slot_mapping=p.slot_mapping,
-                           stream=stream)
+        if self.pcp_ranks <= 0:
+            fused_rmsnorm_rope(p.kv_c, p.k_pe, p.rms_w, p.eps, p.cos_sin, p.positions,
+                               kv_c_out=self.kv_c_out, k_pe_out=self.k_pe_out,
+                               cache=self.cache, cache_scale=self.cache_scale,
+                               slot_mapping=p.slot_mapping, stream=stream)
+            return
+        T = p.kv_c.shape[0]
+        bounds = [T * r // self.pcp_ranks for r in range(self.pcp_ranks + 1)]
+        for a, b in zip(bounds[:-1], bounds[1:]):   # rank r materialises rows [a, b)
+            if b > a:
+                fused_rmsnorm_rope(p.kv_c[a:b], p.k_pe[a:b], p.rms_w, p.eps, p.cos_sin,
+                                   p.positions[a:b], kv_c_out=self.kv_c_out[a:b],
+                                   k_pe_out=self.k_pe_out[a:b], stream=stream)
+        cache_insert(self.kv_c_out, self.k_pe_out, self.cache, p.slot_mapping,
+                     cache_scale=self.cache_scale, stream=stream)
 
     def run_topk(self, stream=None, with_local_idx=False, logits=None):
         topk_select(self.logits if logits is None else logits, self.k, ctx=self.ctx,
