@@ -144,9 +144,9 @@ def main():
         calibrate_copy()
         return
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build emulates every "
-              "shard on a single MI355X; multi-GPU sharding is a design note, not a benchmark.",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): every shard is emulated "
+              "as a slice of one buffer on a single MI355X; sharding across GPUs is described in "
+              "the design notes, not benchmarked.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
