@@ -124,29 +124,31 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int n) {
 // they spread the scores evenly, and the bin holding the k-th best score
 // usually holds only a handful of elements.  The map is monotone in the
 // score order of order_key (NaN and -inf in bin 0, +inf in the last bin;
-// finite scores through a rounded subtract and multiply, both monotone), so
-// "bin above b" implies "key above every key of bin b".
+// finite scores through a rounded fused subtract and a multiply, both
+// monotone), so "bin above b" implies "key above every key of bin b".
 struct LinBins {
-  float lo_half;  // smallest finite score / 2
-  float scale;    // bins per unit of (score / 2); 0 when every score shares one bin
+  float lo_half;  // smallest finite score / 2 (0 when there is none)
+  float scale;    // bins per unit of (score / 2): finite and > 0
 };
 
 __device__ __forceinline__ LinBins make_lin_bins(float vmin, float vmax) {
-  LinBins lb{0.f, 0.f};
+  LinBins lb{0.f, 1.f};
   if (vmin <= vmax) {   // at least one finite score
     lb.lo_half = vmin * 0.5f;
     const float range = vmax * 0.5f - lb.lo_half;  // halves: no overflow
-    const float sc = range > 0.f ? (float)kBins / range : 0.f;
-    lb.scale = sc <= 3.0e38f ? sc : 0.f;           // a range too small to divide
+    if (range > 0.f) lb.scale = fminf((float)kBins / range, 3.0e38f);   // tiny range: fewer bins
   }
   return lb;
 }
 
+// (score/2 - lo_half) * scale, clamped to the table.  Special values need no
+// branch: fmaxf(NaN, 0) is 0, so NaN lands in bin 0 with -inf, and +inf in
+// the last bin, where their order keys rank; the map is monotone in the
+// score, so a bin above b only holds keys above every key of bin b.  Any
+// other value (a slot outside the valid range, counted with weight 0) is
+// clamped into the table.
 __device__ __forceinline__ uint32_t lin_bin(uint32_t bits, LinBins lb) {
-  if ((bits & 0x7f800000u) == 0x7f800000u) return bits == 0x7f800000u ? kBins - 1 : 0u;
-  // t >= 0 for every score >= the minimum; the clamps keep any other value
-  // (a slot outside the valid range, counted with weight 0) inside the table
-  const float t = (__uint_as_float(bits) * 0.5f - lb.lo_half) * lb.scale;
+  const float t = __builtin_fmaf(__uint_as_float(bits), 0.5f, -lb.lo_half) * lb.scale;
   return (uint32_t)fminf(fmaxf(t, 0.f), (float)(kBins - 1));
 }
 
