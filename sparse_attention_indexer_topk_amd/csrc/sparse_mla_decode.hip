@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   constexpr int kSmemB = kMainB > kEpiB ? kMainB : kEpiB;
   __shared__ __attribute__((aligned(16))) uint8_t s_main[kSmemB];
   __shared__ int s_slot[kMaxSel];
-  __shared__ int s_restart;
+  __shared__ int s_restart[2];   // restart requests raised at tiles of each parity
   uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
   uint8_t* s_conv = s_main + kStages * kRingB;
 
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 #pragma unroll
   for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
-  if (tid == 0) s_restart = 0;
+  if (tid < 2) s_restart[tid] = 0;
   lgkm_wait0();
   bar();   // slot list and flag ready (q may still be in flight)
 
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       m_ref = mt;
     } else if (__any(mt > m_ref + kRestartSlack)) {
       m_ref = fmaxf(m_ref, mt);
-      if (lane == 0) s_restart = 1;
+      if (lane == 0) s_restart[tt & 1] = 1;
     }
     const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
     // P^T operand: element e < 4 is token 4*g4 + e, element 4 + e is token
@@ -380,9 +380,11 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // Iteration tt requests tiles up to tt+2 (tile tt+2 goes to the stage of
   // tile tt-2, which every wave left before the previous barrier), waits for
   // tile tt, passes the barrier (every wave is then done with tile tt-1) and
-  // computes tile tt.  A restart request raised while computing tile tt is
-  // seen at the next barrier: inside the loop at the next tile's barrier,
-  // after the last tile at the barrier below the loop.
+  // computes tile tt.  A restart request raised while computing tile tt goes
+  // to flag slot tt % 2 and is read after the next barrier: inside the loop
+  // at the next tile's barrier, after the last tile at the barrier below the
+  // loop.  With two slots, a fast wave raising a request at tile tt never
+  // writes the slot a slower wave may still be reading for tile tt-1.
   int tt = 0;
   int next_issue = 0;
   for (;;) {
@@ -391,12 +393,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     vm_wait_n(my_dma * (next_issue - 1 - tt));
     lgkm_wait0();
     bar();   // tile tt visible; every wave is done with tile tt-1
-    if (s_restart) {
+    if (s_restart[(tt + 1) & 1]) {   // raised at tile tt-1 (slot 1 is clear at tt = 0)
       // a reference max moved by more than 2^64: drop the partial sums and
       // replay the token list (every wave, since the tile ring is shared)
       vm_wait<0>();
       bar();
-      if (tid == 0) s_restart = 0;
+      if (tid < 2) s_restart[tid] = 0;
 #pragma unroll
       for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_part = 0.f;
@@ -415,9 +417,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
   lgkm_wait0();
   bar();
-  if (!s_restart) break;
+  if (!s_restart[(tt + 1) & 1]) break;   // raised at the last tile, ntiles - 1
   bar();
-  if (tid == 0) s_restart = 0;
+  if (tid < 2) s_restart[tid] = 0;
 #pragma unroll
   for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   l_part = 0.f;
