@@ -20,7 +20,7 @@
 //    4-stage ring with tiles t+1 and t+2 in flight while tile t is consumed;
 //    one barrier per tile (tile arrival, which also retires tile t-1);
 //  - the gather lays a tile out in LDS as 36 blocks of 16 tokens x 32
-//    features (tile_off): a score k-step reads one contiguous 1 KB block and a
+//    features: a score k-step reads one contiguous 1 KB block and a
 //    value transpose read 512 contiguous bytes, free of the bank conflicts
 //    that strided row reads meet on this LDS; one gather instruction fills
 //    one block;
@@ -38,9 +38,12 @@
 //    extreme score ranges) restarts the workgroup's token list with the
 //    raised reference — exact, and free of accumulator-wide VALU work in the
 //    hot loop; the denominator sums fp32 probabilities; lse = (m + log2 l) ln 2;
-//  - fp8 e4m3 caches are gathered raw (576 B/row) and widened to bf16 in LDS
-//    with the hardware converter (exact: e4m3 is a subset of bf16); the
-//    per-tensor scale is folded into the score scale and the output;
+//  - fp8 e4m3 caches are gathered raw (576 B/row) into LDS; each wave reads
+//    its operand codes straight from the raw tile (8 bytes per lane, the
+//    value operand by an 8-bit transpose read, half the LDS bytes of a bf16
+//    tile) and widens them to bf16 in registers with the hardware converter
+//    (exact: e4m3 is a subset of bf16); the per-tensor scale is folded into
+//    the score scale and the output;
 //  - split-K: `splits` workgroups share a part's token list, each emitting its
 //    own partial; lse_combine merges them like shards;
 //  - the epilogue stages each wave's normalised outputs in LDS and stores one
@@ -56,6 +59,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / kWave;   // 8
@@ -106,14 +110,50 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
-// Tile layout in LDS: 36 blocks of 1 KB, block (c / 4) * 2 + t / 16 holding
-// tokens 16*(t/16) .. +16 x 16-byte chunks 4*(c/4) .. +4 (32 features), slot
-// (t % 16) + 16 * (c % 4) inside the block.  A score k-step then reads one
-// whole block (lane l: token l % 16, chunk l / 16) and a value transpose read
-// 512 contiguous bytes, so neither meets a bank conflict; one gather
-// instruction fills one block.
-__device__ __forceinline__ int tile_off(int t, int c) {
-  return (((c >> 2) << 1) + (t >> 4)) * 1024 + (((t & 15) + 16 * (c & 3)) << 4);
+// Tile layout in LDS (bf16): 36 blocks of 1 KB, block (c / 4) * 2 + t / 16
+// holding tokens 16*(t/16) .. +16 x 16-byte chunks 4*(c/4) .. +4 (32
+// features), token t, chunk c in slot (t % 16) + 16 * (c % 4).  A score k-step
+// then reads one whole block (lane l: token l % 16, chunk l / 16) and a value
+// transpose read 512 contiguous bytes, so neither meets a bank conflict; one
+// gather instruction fills one block.
+
+// compile-time loop: f(IntC<0>{}) .. f(IntC<N-1>{})
+template <int I> struct IntC { static constexpr int value = I; };
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// ds_read_b64_tr_b8 at LDS byte address addr + OFF.  Written as asm: the
+// compiler guards the builtin form with a full vmcnt wait when it cannot tell
+// the read from the tile gathers still in flight, which would stall every
+// tile on the next two.  The caller waits for the result with lgkm_wait_v.
+template <int OFF>
+__device__ __forceinline__ i32x2_t lds_read_tr8(uint32_t addr) {
+  i32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// wait until at most N LDS operations are in flight; r is passed through the
+// wait so that its uses cannot move above it
+template <int N>
+__device__ __forceinline__ void lgkm_wait_v(i32x2_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
+}
+
+// 8 e4m3 codes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ bf16x8_t widen8(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4_t cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <bool FP8, bool OFF32>
@@ -125,14 +165,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   constexpr int kRingB = FP8 ? kTileB8 : kTileB;
   constexpr int kDmaTotal = FP8 ? kDmaFp8Total : kDmaBf16Total;
   constexpr int kDmaMax = (kDmaTotal + kAttnWaves - 1) / kAttnWaves;
-  constexpr int kConvB = FP8 ? kTileB : 0;
-  constexpr int kMainB = kStages * kRingB + kConvB;
+  constexpr int kMainB = kStages * kRingB;
   constexpr int kSmemB = kMainB > kEpiB ? kMainB : kEpiB;
   __shared__ __attribute__((aligned(16))) uint8_t s_main[kSmemB];
   __shared__ int s_slot[kMaxSel];
   __shared__ int s_restart[2];   // restart requests raised at tiles of each parity
   uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
-  uint8_t* s_conv = s_main + kStages * kRingB;
 
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin in launch
   // order, so the G = gridDim.y * gridDim.z workgroups of a row (its parts,
@@ -238,6 +276,27 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // 2fb + (s%4)/2, half s%2, so the offset is pv_base + 2048*(fb/2) +
   // 512*(fb%2) + 1024*rd
   const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
+  // ---- the same inside a raw fp8 tile --------------------------------------
+  // The raw tile keeps the block structure of the bf16 one with 16-code
+  // chunks: block 2*(c/4) + t/16 holds tokens 16*(t/16) .. +16 x chunks
+  // 4*(c/4) .. +4, and token t sits in slot ((t % 16) ^ (8 * (t/16))) +
+  // 16 * (c % 4) (the xor keeps the two token halves that one transpose read
+  // touches on different banks).
+  //  - scores, k-step kk (chunks 2kk, 2kk+1), token block b: lane (n16, g4)
+  //    reads the 8 codes of features 32kk + 8*g4 .. +8 of token 16b + n16 at
+  //    qk8_base[b] + 2048*(kk/2) + 512*(kk%2): each 32-lane half of the wave
+  //    reads 256 contiguous bytes;
+  //  - values, block fb (chunk fb): ds_read_b64_tr_b8 hands lane i of a
+  //    16-lane group byte i%8 of the 8-byte chunk addressed by lane 2e + i/8
+  //    of its group as element e, so lane (s, g4) addresses half s%2 of the
+  //    token that element s/2 stands for (4*g4 + e%4, + 16 for e >= 4), at
+  //    pv8_base + 2048*(fb/4) + 256*(fb%4); lane i then holds feature i of
+  //    the block for the 8 tokens in the order of the P^T operand.
+  const int qk8_base0 = 16 * n16 + 256 * (g4 >> 1) + 8 * (g4 & 1);
+  const int qk8_base1 = 1024 + 16 * (n16 ^ 8) + 256 * (g4 >> 1) + 8 * (g4 & 1);
+  const int pv8_e = n16 >> 1;
+  const int pv8_base = 1024 * (pv8_e >> 2) + 16 * ((4 * g4 + (pv8_e & 3)) ^ (8 * (pv8_e >> 2))) +
+                       8 * (n16 & 1);
 
   // ---- DMA issue of tile tt into its ring stage -------------------------------
   // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
@@ -256,7 +315,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       if (ins < kDmaTotal) {
         // instruction ins fills block ins: tokens 16*(ins%2) + lane%16, 16-byte
         // chunks 4*(ins/2) + lane/16 (bf16: 8 features; raw fp8: 16 features)
-        const int t = 16 * (ins & 1) + (lane & 15);
+        // (fp8: token half 1 stored with the slot xor described above)
+        const int t = 16 * (ins & 1) + ((lane & 15) ^ (FP8 ? 8 * (ins & 1) : 0));
         offv[jj] = (4 * (ins >> 1) + (lane >> 4)) * 16;
         const int ti = tbase + t < n_tok ? tbase + t : 0;
         sv[jj] = s_slot[ti];
@@ -283,20 +343,31 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 
   // ---- one tile: scores, softmax, values -------------------------------------
   auto compute = [&](int tt) {
-    const uint8_t* tile = FP8 ? s_conv : s_ring[tt % kStages];
+    const uint8_t* tile = s_ring[tt % kStages];
     const int tbase = tt * kTile;
     const uint32_t vmask = (uint32_t)__ballot(lane < kTile && tbase + lane < n_tok &&
                                               s_slot[tbase + (lane & 31)] >= 0);
     if (!wave_on) return;
     // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
 #pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) {
-      const uint8_t* a = tile + 2048 * kk + 16 * lane;
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 1024);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        const int ko = 2048 * (kk >> 1) + 512 * (kk & 1);
+        const uint2 r0 = *reinterpret_cast<const uint2*>(tile + qk8_base0 + ko);
+        const uint2 r1 = *reinterpret_cast<const uint2*>(tile + qk8_base1 + ko);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(r0.x, r0.y), qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(r1.x, r1.y), qf[kk], s1, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        const uint8_t* a = tile + 2048 * kk + 16 * lane;
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 1024);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
+      }
     }
     // lane holds head `head`, tokens 4*g4 + i (s0) and 16 + 4*g4 + i (s1)
     if (vmask != 0xffffffffu) {
@@ -331,48 +402,39 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     }
     // O^T += V^T P^T, 16 output features per block: ds_read_b64_tr_b16 gives
     // lane (g4, n16) element e = V[token 4*g4 + e (+16)][16*fb + n16]
-    auto vfrag = [&](int fb) {
-      const uint8_t* b = tile + pv_base + 2048 * (fb >> 1) + 512 * (fb & 1);
-      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b));
-      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 1024));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8_t va = vfrag(0);
-#pragma unroll
-    for (int fb = 0; fb < kOBlocks; ++fb) {
-      bf16x8_t nb = va;
-      if (fb + 1 < kOBlocks) nb = vfrag(fb + 1);   // next block's fragment in flight
-      o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[fb], 0, 0, 0);
-      if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-      va = nb;
-    }
-  };
-
-  // fp8: widen raw tile tt into the bf16 tile layout of s_conv.  The raw tile
-  // holds 18 blocks of 16 tokens x 4 chunks of 16 codes in gather order, so a
-  // thread reads one contiguous 16-byte slot and its two bf16 chunks land in
-  // slots that consecutive threads fill contiguously.
-  auto widen = [&](int tt) {
     if constexpr (FP8) {
-      const uint8_t* raw8 = s_ring[tt % kStages];
-      for (int d = tid; d < kTileB8 / 16; d += kAttnThreads) {
-        const int blk = d >> 6, l = d & 63;
-        const int tr = 16 * (blk & 1) + (l & 15);
-        const int rc = 4 * (blk >> 1) + (l >> 4);    // codes 16*rc .. +16
-        const uint4 rw = *reinterpret_cast<const uint4*>(raw8 + d * 16);
-        const uint32_t w[4] = {rw.x, rw.y, rw.z, rw.w};
-        uint32_t h[8];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, false);
-          const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q4], 1.0f, true);
-          h[2 * q4] = __builtin_bit_cast(uint32_t, lo);
-          h[2 * q4 + 1] = __builtin_bit_cast(uint32_t, hi);
+      // raw codes of the next block in flight while the current one is
+      // widened and multiplied
+      const uint32_t pv8 = (uint32_t)(uintptr_t)(lds_void_ptr)(tile + pv8_base);
+      i32x2_t r[kOBlocks];
+      r[0] = lds_read_tr8<0>(pv8);
+      static_for<kOBlocks>([&](auto fbc) {
+        constexpr int fb = decltype(fbc)::value;
+        if constexpr (fb + 1 < kOBlocks) {
+          r[fb + 1] = lds_read_tr8<2048 * ((fb + 1) >> 2) + 256 * ((fb + 1) & 3)>(pv8);
+          lgkm_wait_v<1>(r[fb]);
+        } else {
+          lgkm_wait_v<0>(r[fb]);
         }
-        *reinterpret_cast<uint4*>(s_conv + tile_off(tr, 2 * rc)) =
-            make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(s_conv + tile_off(tr, 2 * rc + 1)) =
-            make_uint4(h[4], h[5], h[6], h[7]);
+        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            widen8((uint32_t)r[fb].x, (uint32_t)r[fb].y), pf, o[fb], 0, 0, 0);
+        if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+      auto vfrag = [&](int fb) {
+        const uint8_t* b = tile + pv_base + 2048 * (fb >> 1) + 512 * (fb & 1);
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 1024));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t va = vfrag(0);
+#pragma unroll
+      for (int fb = 0; fb < kOBlocks; ++fb) {
+        bf16x8_t nb = va;
+        if (fb + 1 < kOBlocks) nb = vfrag(fb + 1);   // next block's fragment in flight
+        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[fb], 0, 0, 0);
+        if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        va = nb;
       }
     }
   };
@@ -406,11 +468,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       tt = 0;
       next_issue = 0;
       continue;
-    }
-    if constexpr (FP8) {
-      widen(tt);
-      lgkm_wait0();
-      bar();
     }
     compute(tt);
     ++tt;
