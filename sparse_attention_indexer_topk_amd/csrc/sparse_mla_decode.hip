@@ -341,15 +341,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // this wave's DMA instructions per tile
   const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  // ---- one tile: scores, softmax, values -------------------------------------
-  auto compute = [&](int tt) {
+  // ---- one tile, first half: scores -------------------------------------------
+  // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
+  auto scores = [&](int tt, f32x4_t& s0, f32x4_t& s1) {
     const uint8_t* tile = s_ring[tt % kStages];
-    const int tbase = tt * kTile;
-    const uint32_t vmask = (uint32_t)__ballot(lane < kTile && tbase + lane < n_tok &&
-                                              s_slot[tbase + (lane & 31)] >= 0);
+    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (!wave_on) return;
-    // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
 #pragma unroll
       for (int kk = 0; kk < kQSteps; ++kk) {
@@ -369,6 +367,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
       }
     }
+  };
+
+  // ---- one tile, second half: mask, softmax, values ----------------------------
+  // sv: the slot entry of token lane % 32 of the tile, read without a bound
+  // (the list has room for every tile); tokens past the tile's end are masked
+  // by position
+  auto finish = [&](int tt, int sv, f32x4_t s0, f32x4_t s1) {
+    const uint8_t* tile = s_ring[tt % kStages];
+    const int tbase = tt * kTile;
+    const uint32_t vmask = (uint32_t)__ballot(lane < kTile && tbase + lane < n_tok && sv >= 0);
+    if (!wave_on) return;
     // lane holds head `head`, tokens 4*g4 + i (s0) and 16 + 4*g4 + i (s1)
     if (vmask != 0xffffffffu) {
 #pragma unroll
@@ -379,8 +388,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     }
     float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                      fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * qk_scale;
+    // max over the head's four lanes (n16 + 16j): swap 16-lane rows 0<->1 and
+    // 2<->3, then the two 32-lane halves; each swap returns both operands,
+    // whose max is the pairwise max in every lane
+    {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                      false, false);
+      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                      false, false);
+      mt = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) * qk_scale;
+    }
     if (m_ref == -INFINITY) {
       m_ref = mt;
     } else if (__any(mt > m_ref + kRestartSlack)) {
@@ -455,7 +473,14 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     vm_wait_n(my_dma * (next_issue - 1 - tt));
     lgkm_wait0();
     bar();   // tile tt visible; every wave is done with tile tt-1
-    if (s_restart[(tt + 1) & 1]) {   // raised at tile tt-1 (slot 1 is clear at tt = 0)
+    // the restart flag raised at tile tt-1 (slot 1 is clear at tt = 0) and the
+    // tile's slot entries are requested here and first used after the score
+    // products, which change nothing that a restart keeps
+    const int rflag = s_restart[(tt + 1) & 1];
+    const int sv = s_slot[tt * kTile + (lane & 31)];
+    f32x4_t s0, s1;
+    scores(tt, s0, s1);
+    if (__builtin_amdgcn_readfirstlane(rflag)) {
       // a reference max moved by more than 2^64: drop the partial sums and
       // replay the token list (every wave, since the tile ring is shared)
       vm_wait<0>();
@@ -469,7 +494,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       next_issue = 0;
       continue;
     }
-    compute(tt);
+    finish(tt, sv, s0, s1);
     ++tt;
   }
   lgkm_wait0();
