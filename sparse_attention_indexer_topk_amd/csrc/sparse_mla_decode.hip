@@ -137,6 +137,27 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+// ds_read_b64_tr_b16 at LDS byte address addr + OFF, for the same reason
+template <int OFF>
+__device__ __forceinline__ i32x2_t lds_read_tr16(uint32_t addr) {
+  i32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// ds_read_b128 at LDS byte address addr + OFF (as above: the compiler would
+// guard it with a full vmcnt wait behind the tile gathers in flight)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// wait until at most N LDS operations are in flight, passing a and b through
+template <int N>
+__device__ __forceinline__ void lgkm_wait_2(u32x4_t& a, u32x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
 // wait until at most N LDS operations are in flight; r is passed through the
 // wait so that its uses cannot move above it
 template <int N>
@@ -558,6 +579,380 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
 }
 
+// ---- bf16 caches: the waves share the probabilities through LDS ---------------
+// Score phase as above (a wave: 16 heads x all 576 features, q in registers).
+// Value phase split by output features instead of heads: wave w owns features
+// 64w .. 64w+63 for all 128 heads, so it reads 4 value fragments per tile
+// instead of 32 and takes the 8 heads blocks' P^T operands (1 KB each) that
+// the score waves wrote to LDS.  The LDS bytes a tile costs drop from
+// 8 x (36 + 32) KB to 8 x (36 + 4 + 8) + 8 KB.  Pipelining:
+//  - iteration t: wait for tile t, barrier, request tile t+2, values of tile
+//    t-1 (its P^T written in iteration t-1, double-buffered by tile parity),
+//    scores and softmax of tile t, P^T of tile t to LDS;
+//  - the ring keeps features 0..511 of 4 tiles (t-1 for values, t for scores,
+//    t+1 and t+2 in flight) and features 512..575 of 3 (t, t+1, t+2);
+//  - the slot list is not staged whole: a ring of 8 tiles' entries is refilled
+//    by an HBM->LDS copy that rides with the gathers of the tile 3 earlier, so
+//    the wait for that tile covers it and its barrier publishes it.
+// The output scale 1/l of each head is handed from its score wave to the
+// value waves through LDS after the last tile.
+constexpr int kSpMainB = 32 * 1024;             // features 0..511 of a tile
+constexpr int kSpRopeB = 4 * 1024;              // features 512..575
+constexpr int kSpMainStages = 4;
+constexpr int kSpRopeStages = 3;
+constexpr int kSpTilesB = kSpMainStages * kSpMainB + kSpRopeStages * kSpRopeB;
+constexpr int kSpPB = kTile * kHPB * 2;         // P^T of one tile, 128 heads (8 KB)
+constexpr int kSpSlotRing = 8;                  // tiles of slot entries held in LDS
+constexpr int kSpSlotInit = 4;                  // tiles whose entries are loaded at startup
+constexpr int kSpRefillWave = 7;                // has 4 gathers per tile, the others 4 or 5
+constexpr int kSpFBW = kValue / 16 / kAttnWaves;   // 4 output feature blocks per wave
+constexpr int kSpNHB = kHPB / 16;                  // 8 head blocks
+static_assert(kHPB * kEpiRow <= kSpTilesB, "epilogue staging fits in the tile ring");
+static_assert(kDmaBf16Total == 36 && kSpMainB / 1024 == 32, "32 main + 4 rope blocks per tile");
+
+// the lane index, recomputed where it is used: values derived from it are
+// then rebuilt in two instructions instead of being held across the tile loop
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+template <bool OFF32>
+__global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
+    const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
+    int64_t num_slots, const int* __restrict__ slots, const int* __restrict__ counts, int k,
+    int splits, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kDmaMax = (kDmaBf16Total + kAttnWaves - 1) / kAttnWaves;   // 5
+  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kSpTilesB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kSpPB];
+  __shared__ __attribute__((aligned(16))) int s_sring[kSpSlotRing * kTile];
+  __shared__ float s_inv[kHPB];
+  __shared__ int s_restart[2];
+
+  int row, yz;   // XCD-aware order, as in the kernel above
+  {
+    const int G = gridDim.y * gridDim.z;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int b = L / (8 * G), w = L % (8 * G);
+    const int nr = rows - 8 * b < 8 ? rows - 8 * b : 8;
+    row = 8 * b + w % nr;
+    yz = w / nr;
+  }
+  const int part = (yz % gridDim.y) / splits;
+  const int split = (yz % gridDim.y) % splits;
+  const int hg = yz / gridDim.y;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int h0 = hg * kHPB + wave * kHPW;
+  const int head = h0 + n16;
+  const bool wave_on = h0 < heads;   // heads is a multiple of 16
+  const int n_hb = (heads - hg * kHPB) / 16 < kSpNHB ? (heads - hg * kHPB) / 16 : kSpNHB;
+  const int out_part = yz % gridDim.y;
+  const int slot_lim = num_slots > 0x7fffffffLL ? 0x7fffffff : (int)num_slots;
+
+  // ---- startup: count, the first tiles' slot entries, q -------------------------
+  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
+  int cnt = counts ? counts[(int64_t)part * rows + row] : k;
+  bf16x8_t qf[kQSteps];   // loaded after the first gathers are issued
+  int sl0 = 0;
+  if (splits == 1 && tid < kSpSlotInit * kTile) sl0 = my_slots[tid];   // k >= 512
+  cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
+  if (num_slots <= 0) cnt = 0;
+  const int per = ((cnt + splits - 1) / splits + kTile - 1) / kTile * kTile;
+  const int t_lo = split * per < cnt ? split * per : cnt;
+  const int t_hi = t_lo + per < cnt ? t_lo + per : cnt;
+  const int n_tok = t_hi - t_lo;
+  const int ntiles = (n_tok + kTile - 1) / kTile;
+  auto load_first_slots = [&](bool have) {
+    if (tid < kSpSlotInit * kTile) {
+      int s = sl0;
+      if (!have) {
+        const int i = t_lo + tid;
+        s = my_slots[i < k ? i : k - 1];
+      }
+      s_sring[tid] = s;
+    }
+  };
+  load_first_slots(splits == 1);
+
+  f32x4_t o[kSpFBW][kSpNHB];
+#pragma unroll
+  for (int f = 0; f < kSpFBW; ++f)
+#pragma unroll
+    for (int hb = 0; hb < kSpNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = sm_scale * kLog2e;
+  float m_ref = -INFINITY, l_part = 0.f;
+  if (tid < 2) s_restart[tid] = 0;
+  lgkm_wait0();
+  bar();   // first slot entries and flags ready
+
+  const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
+  auto main_stage = [&](int tt) { return s_tiles + (tt & (kSpMainStages - 1)) * kSpMainB; };
+  auto rope_stage = [&](int tt) {
+    return s_tiles + kSpMainStages * kSpMainB + (tt % kSpRopeStages) * kSpRopeB;
+  };
+  // this wave's vector-memory operations for tile u: its gathers, and for the
+  // refill wave the copy of tile u+3's slot entries
+  const int my_dma = kDmaBf16Total / kAttnWaves + (wave < kDmaBf16Total % kAttnWaves ? 1 : 0);
+  auto refills = [&](int u) {
+    return wave == kSpRefillWave && u + 3 >= kSpSlotInit && u + 3 < ntiles;
+  };
+  auto tile_slots = [&](int u, int (&sv)[kDmaMax]) {
+#pragma unroll
+    for (int jj = 0; jj < kDmaMax; ++jj) {
+      const int ins = jj * kAttnWaves + wave;
+      sv[jj] = 0;
+      if (ins < kDmaBf16Total)
+        sv[jj] = s_sring[(u & (kSpSlotRing - 1)) * kTile + 16 * (ins & 1) + (lane & 15)];
+    }
+  };
+  // block ins of tile u: tokens 16*(ins%2) + lane%16, 16-byte chunks 4*(ins/2)
+  // + lane/16; blocks 0..31 go to the main stage, 32..35 to the rope stage
+  auto issue = [&](int u, const int (&sv)[kDmaMax]) {
+    if (refills(u) && lane < kTile) {
+      const int i = t_lo + (u + 3) * kTile + lane_now();
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(my_slots + (i < k ? i : k - 1)),
+          (lds_void_ptr)(s_sring + ((u + 3) & (kSpSlotRing - 1)) * kTile), 4, 0, 0);
+    }
+    uint8_t* ms = main_stage(u);
+    uint8_t* rs = rope_stage(u);
+#pragma unroll
+    for (int jj = 0; jj < kDmaMax; ++jj) {
+      const int ins = jj * kAttnWaves + wave;
+      if (ins < kDmaBf16Total) {
+        const int off = (4 * (ins >> 1) + (lane >> 4)) * 16;
+        const int s = (unsigned)sv[jj] < (unsigned)slot_lim ? sv[jj] : 0;
+        const uint8_t* src;
+        if constexpr (OFF32)
+          src = cache + (uint32_t)((uint32_t)s * (uint32_t)kRowB + (uint32_t)off);
+        else
+          src = cache + (int64_t)s * kRowB + off;
+        uint8_t* dst = ins < 32 ? ms + ins * 1024 : rs + (ins - 32) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)dst, 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
+  // the key operands of k-step kk (token blocks 0..15 and 16..31) are read
+  // two k-steps ahead of their products
+  auto scores = [&](int tt, f32x4_t& s0, f32x4_t& s1) {
+    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (!wave_on) return;
+    const uint32_t ma = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 16 * lane);
+    const uint32_t ra = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + 16 * lane);
+    u32x4_t ka[kQSteps], kb[kQSteps];
+    auto rd = [&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if constexpr (kk < 16) {
+        ka[kk] = lds_read_b128<2048 * kk>(ma);
+        kb[kk] = lds_read_b128<2048 * kk + 1024>(ma);
+      } else {
+        ka[kk] = lds_read_b128<2048 * (kk - 16)>(ra);
+        kb[kk] = lds_read_b128<2048 * (kk - 16) + 1024>(ra);
+      }
+    };
+    rd(IntC<0>{});
+    rd(IntC<1>{});
+    static_for<kQSteps>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if constexpr (kk + 1 < kQSteps) lgkm_wait_2<2>(ka[kk], kb[kk]);
+      else lgkm_wait_2<0>(ka[kk], kb[kk]);
+      if constexpr (kk + 2 < kQSteps) rd(IntC<kk + 2>{});
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[kk]), qf[kk], s0,
+                                                   0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[kk]), qf[kk], s1,
+                                                   0, 0, 0);
+    });
+  };
+
+  // O^T += V^T P^T for this wave's 4 feature blocks and every present head
+  // block; the P^T of head block hb is what lane `lane` of score wave hb wrote
+  auto values = [&](int tt) {
+    const uint32_t vb =
+        (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv_base + 4096 * wave);
+    const uint8_t* pb = s_p[tt & 1] + 16 * lane;
+    // the 4 value fragments: ds_read_b64_tr_b16 of features 16*(4*wave + f) +
+    // lane%16 for tokens 4*g4 + e (first read) and 16 + 4*g4 + e (second)
+    i32x2_t r[2 * kSpFBW];
+    static_for<kSpFBW>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      r[2 * f] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1)>(vb);
+      r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1) + 1024>(vb);
+    });
+    bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pb);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                   "+v"(r[6]), "+v"(r[7]));
+    bf16x8_t va[kSpFBW];
+#pragma unroll
+    for (int f = 0; f < kSpFBW; ++f)
+      va[f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2, 3));
+#pragma unroll
+    for (int hb = 0; hb < kSpNHB; ++hb) {
+      if (hb < n_hb) {
+        bf16x8_t pn = pa;
+        if (hb + 1 < n_hb) pn = *reinterpret_cast<const bf16x8_t*>(pb + 1024 * (hb + 1));
+#pragma unroll
+        for (int f = 0; f < kSpFBW; ++f)
+          o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
+        pa = pn;
+      }
+    }
+  };
+
+  // mask, softmax against the reference max, P^T of tile tt to LDS
+  auto finish = [&](int tt, int sv, f32x4_t s0, f32x4_t s1) {
+    const int tbase = tt * kTile;
+    const int ln = lane_now();
+    const uint32_t vmask = (uint32_t)__ballot(ln < kTile && tbase + ln < n_tok &&
+                                              (unsigned)sv < (unsigned)slot_lim);
+    if (!wave_on) return;
+    if (vmask != 0xffffffffu) {
+      const uint32_t mv = vmask >> (4 * (lane_now() >> 4));   // bit i: token 4*g4 + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s0[i] = (mv >> i) & 1u ? s0[i] : -INFINITY;
+        s1[i] = (mv >> (16 + i)) & 1u ? s1[i] : -INFINITY;
+      }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                      false, false);
+      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                      false, false);
+      mt = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) * qk_scale;
+    }
+    if (m_ref == -INFINITY) {
+      m_ref = mt;
+    } else if (__any(mt > m_ref + kRestartSlack)) {
+      m_ref = fmaxf(m_ref, mt);
+      if (lane == 0) s_restart[tt & 1] = 1;
+    }
+    const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    bf16x8_t pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], qk_scale, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], qk_scale, nm));
+      l_part += p0;
+      l_part += p1;
+      pf[i] = static_cast<__bf16>(p0);
+      pf[4 + i] = static_cast<__bf16>(p1);
+    }
+    *reinterpret_cast<bf16x8_t*>(s_p[tt & 1] + (wave * kWave + lane_now()) * 16) = pf;
+  };
+
+  // both tiles' slot entries are read before the first gather is issued
+  auto start = [&]() {
+    int sv0[kDmaMax], sv1[kDmaMax];
+    tile_slots(0, sv0);
+    tile_slots(1, sv1);
+    if (ntiles > 0) issue(0, sv0);
+    if (ntiles > 1) issue(1, sv1);
+  };
+  start();
+  // q (the B operand of the score products) is requested after the first two
+  // tiles' gathers, and everything in flight is waited for before the loop,
+  // so that inside it q is known to be in registers
+  const uint16_t* qp = q + ((int64_t)row * heads + (wave_on ? head : 0)) * kLatent + 8 * g4;
+#pragma unroll
+  for (int kk = 0; kk < kQSteps; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
+  // the wait passes q through, so the loop sees q as plain registers
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
+                 "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]),
+                 "+v"(qf[12]), "+v"(qf[13]), "+v"(qf[14]), "+v"(qf[15]), "+v"(qf[16]),
+                 "+v"(qf[17])
+               :
+               : "memory");
+  // A restart request raised while finishing tile t goes to flag slot t % 2
+  // and is read after the next barrier, in iteration t+1 (the last tile's in
+  // the extra iteration t = ntiles, which only finishes the values).
+  for (int t = 0; t <= ntiles;) {
+    if (t + 1 < ntiles) vm_wait_n(my_dma + (refills(t + 1) ? 1 : 0));
+    else vm_wait<0>();
+    lgkm_wait0();
+    bar();   // tile t visible; P^T of tile t-1 written; every wave done with tile t-2
+    const int rflag = s_restart[(t + 1) & 1];
+    const int sv = t < ntiles ? s_sring[(t & (kSpSlotRing - 1)) * kTile + (lane & 31)] : 0;
+    if (t + 2 < ntiles) {
+      int nsv[kDmaMax];
+      tile_slots(t + 2, nsv);
+      issue(t + 2, nsv);
+    }
+    if (t >= 1) values(t - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t s0, s1;
+    if (t < ntiles) scores(t, s0, s1);
+    if (__builtin_amdgcn_readfirstlane(rflag)) {
+      // a reference max moved by more than 2^64: drop the partial sums and
+      // replay the token list with the raised reference
+      vm_wait<0>();
+      lgkm_wait0();
+      bar();
+      if (tid < 2) s_restart[tid] = 0;
+#pragma unroll
+      for (int f = 0; f < kSpFBW; ++f)
+#pragma unroll
+        for (int hb = 0; hb < kSpNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      l_part = 0.f;
+      load_first_slots(false);
+      __syncthreads();
+      start();
+      t = 0;
+      continue;
+    }
+    if (t < ntiles) finish(t, sv, s0, s1);
+    ++t;
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  if (wave_on && g4 == 0) {
+    s_inv[wave * kHPW + n16] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    lse[((int64_t)out_part * rows + row) * heads + head] = lv;
+  }
+  lgkm_wait0();
+  bar();   // 1/l of every head published; every wave done with the ring
+#pragma unroll
+  for (int hb = 0; hb < kSpNHB; ++hb) {
+    if (hb < n_hb) {
+      const float inv = s_inv[16 * hb + n16];
+      uint8_t* stg = s_tiles + (16 * hb + n16) * kEpiRow + (64 * wave + 4 * g4) * 2;
+#pragma unroll
+      for (int f = 0; f < kSpFBW; ++f) {
+        const uint2 v = make_uint2(pack_bf16x2(o[f][hb][0] * inv, o[f][hb][1] * inv),
+                                   pack_bf16x2(o[f][hb][2] * inv, o[f][hb][3] * inv));
+        *reinterpret_cast<uint2*>(stg + 32 * f) = v;
+      }
+    }
+  }
+  lgkm_wait0();
+  bar();
+  if (wave_on) {
+    uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue;
+#pragma unroll
+    for (int r = 0; r < kHPW; ++r) {
+      const uint4 v = *reinterpret_cast<const uint4*>(s_tiles + (wave * kHPW + r) * kEpiRow + lane * 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + lane * 16) = v;
+    }
+  }
+}
+
 int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cache, bool fp8,
                              const float* cache_scale, int64_t num_slots, const int* slots,
                              const int* counts, int k, int n_parts, int splits, float sm_scale,
@@ -576,8 +971,14 @@ int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cac
     if (off32) DSA_ATTN(true, true);
     else DSA_ATTN(true, false);
   } else {
-    if (off32) DSA_ATTN(false, true);
-    else DSA_ATTN(false, false);
+    if (off32)
+      hipLaunchKernelGGL((sparse_mla_decode_bf16_kernel<true>), grid, dim3(kAttnThreads), 0,
+                         stream, q16, rows, heads, c8, num_slots, slots, counts, k, splits,
+                         sm_scale, o16, lse);
+    else
+      hipLaunchKernelGGL((sparse_mla_decode_bf16_kernel<false>), grid, dim3(kAttnThreads), 0,
+                         stream, q16, rows, heads, c8, num_slots, slots, counts, k, splits,
+                         sm_scale, o16, lse);
   }
 #undef DSA_ATTN
   return 0;
