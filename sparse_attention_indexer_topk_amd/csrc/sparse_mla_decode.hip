@@ -9,27 +9,30 @@
 //   lse = ln sum_j exp(s_j).
 //
 // How (gfx950, one workgroup = 8 waves = 128 heads of one (row, part, split)):
-//  - each wave owns 16 heads over all 576 features: q (the B operand of
-//    v_mfma_f32_16x16x32_bf16, 18 k-steps) stays in 72 VGPRs and the output
-//    (32 blocks of 16 x 16 fp32) in 128, so waves need no partial-score
-//    exchange and the key tile enters LDS once for all 128 heads;
-//  - the part's slot list is staged once in LDS; the selected latent rows are
-//    gathered 32 tokens per tile straight from HBM into LDS with
-//    global_load_lds_dwordx4 (no register staging; a uniform base plus a
-//    32-bit offset per lane when the pool spans less than 4 GiB) through a
-//    4-stage ring with tiles t+1 and t+2 in flight while tile t is consumed;
-//    one barrier per tile (tile arrival, which also retires tile t-1);
-//  - the gather lays a tile out in LDS as 36 blocks of 16 tokens x 32
-//    features: a score k-step reads one contiguous 1 KB block and a
-//    value transpose read 512 contiguous bytes, free of the bank conflicts
-//    that strided row reads meet on this LDS; one gather instruction fills
-//    one block;
+//  - score phase: each wave owns 16 heads over all 576 features; q (the B
+//    operand of v_mfma_f32_16x16x32_bf16, 18 k-steps) stays in 72 VGPRs and
+//    the key tile enters LDS once for all 128 heads;
+//  - value phase, split by output features instead: wave w owns features
+//    64w .. 64w+63 for all 128 heads (32 blocks of 16 x 16 fp32 in 128
+//    VGPRs), so it reads 4 value fragments per tile and takes the P^T
+//    operands of the 8 head blocks (1 KB each) that the score waves wrote to
+//    LDS; per tile every wave reads the whole key tile once, but only an
+//    eighth of the value tile;
+//  - the selected latent rows are gathered 32 tokens per tile straight from
+//    HBM into LDS with global_load_lds_dwordx4 (no register staging; a
+//    uniform base plus a 32-bit offset per lane when the pool spans less
+//    than 4 GiB); one barrier per tile;
+//  - the gather lays a tile out in LDS as blocks of 16 tokens x 16-byte
+//    chunks (1 KB): a score k-step reads one contiguous block and a value
+//    transpose read contiguous bytes, free of the bank conflicts that
+//    strided row reads meet on this LDS; one gather instruction fills one
+//    block;
 //  - scores are computed transposed, S^T = K Q^T (rows = tokens), so each
 //    lane ends with 8 tokens of ONE head — with the token order inside the
 //    k dimension permuted the same way on both operands, exactly the B
-//    operand (P^T) of the value product O^T += V^T P^T; V^T fragments are
-//    read from the row-major tile with ds_read_b64_tr_b16 (LDS transpose
-//    read), the next block's while the current block's MFMA runs;
+//    operand (P^T) of the value product O^T += V^T P^T, which the score wave
+//    stores as is; V^T fragments come from the row-major tile through the
+//    LDS transpose reads;
 //  - softmax in base 2 (v_exp_f32 computes 2^x) against a reference max
 //    fixed by the first tile: probabilities may exceed 1 by up to 2^64, which
 //    fp32 accumulators and bf16 operands hold exactly as well as values near
@@ -40,14 +43,14 @@
 //    hot loop; the denominator sums fp32 probabilities; lse = (m + log2 l) ln 2;
 //  - fp8 e4m3 caches are gathered raw (576 B/row) into LDS; each wave reads
 //    its operand codes straight from the raw tile (8 bytes per lane, the
-//    value operand by an 8-bit transpose read, half the LDS bytes of a bf16
-//    tile) and widens them to bf16 in registers with the hardware converter
-//    (exact: e4m3 is a subset of bf16); the per-tensor scale is folded into
-//    the score scale and the output;
+//    value operand by an 8-bit transpose read) and widens them to bf16 in
+//    registers with the hardware converter (exact: e4m3 is a subset of
+//    bf16); the per-tensor scale is folded into the score scale and the
+//    output;
 //  - split-K: `splits` workgroups share a part's token list, each emitting its
 //    own partial; lse_combine merges them like shards;
-//  - the epilogue stages each wave's normalised outputs in LDS and stores one
-//    whole 1 KB head row per instruction.
+//  - the epilogue stages the normalised outputs in LDS and stores one whole
+//    1 KB head row per instruction.
 #include "launchers.h"
 
 namespace dsa {
@@ -66,26 +69,18 @@ constexpr int kAttnWaves = kAttnThreads / kWave;   // 8
 constexpr int kHPW = 16;                       // heads per wave
 constexpr int kHPB = kHPW * kAttnWaves;        // heads per block (128)
 constexpr int kTile = 32;                      // tokens per tile
-constexpr int kStages = 4;                     // tiles in the LDS ring
 constexpr int kRowB = kLatent * 2;             // bf16 row bytes (1152)
 constexpr int kTileB = kTile * kRowB;          // 36864 bytes
 constexpr int kRowB8 = kLatent;                // fp8 row bytes (576)
 constexpr int kTileB8 = kTile * kRowB8;        // 18432 bytes
 constexpr int kQSteps = kLatent / 32;          // 18 k-steps of 32 features
-constexpr int kOBlocks = kValue / 16;          // 32 blocks of 16 output features
-constexpr int kMaxSel = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRestartSlack = 64.0f;         // log2 units
 // epilogue staging: each wave's 16 heads x 512 bf16 outputs, rows padded by
 // 16 bytes so that the row-strided 8-byte writes spread over the banks
 constexpr int kEpiRow = kValue * 2 + 16;
-constexpr int kEpiWaveB = kHPW * kEpiRow;
-constexpr int kEpiB = kAttnWaves * kEpiWaveB;
 
-// DMA instructions (64 lanes x 16 B) per tile, dealt round-robin to the waves
-constexpr int kDmaBf16Total = kTileB / (16 * kWave);           // 36
-constexpr int kDmaFp8Total = kTileB8 / (16 * kWave);           // 18
 
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 // wait until at most N vector-memory operations of this wave are in flight
@@ -97,13 +92,14 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ void vm_wait_n(int n) {
   switch (n) {
     case 0: vm_wait<0>(); break;
+    case 1: vm_wait<1>(); break;
     case 2: vm_wait<2>(); break;
     case 3: vm_wait<3>(); break;
     case 4: vm_wait<4>(); break;
     case 5: vm_wait<5>(); break;
     case 6: vm_wait<6>(); break;
+    case 7: vm_wait<7>(); break;
     case 8: vm_wait<8>(); break;
-    case 10: vm_wait<10>(); break;
     default: vm_wait<0>(); break;   // any other count: wait for everything
   }
 }
@@ -158,6 +154,21 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait_2(u32x4_t& a, u32x4_t& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
+// ds_read_b64 at LDS byte address addr + OFF
+template <int OFF>
+__device__ __forceinline__ i32x2_t lds_read_b64(uint32_t addr) {
+  i32x2_t r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_2v(i32x2_t& a, i32x2_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_4v(i32x2_t& a, i32x2_t& b, i32x2_t& c, i32x2_t& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
 // wait until at most N LDS operations are in flight; r is passed through the
 // wait so that its uses cannot move above it
 template <int N>
@@ -177,21 +188,81 @@ __device__ __forceinline__ bf16x8_t widen8(uint32_t w0, uint32_t w1) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---- pipelining and LDS layout ----------------------------------------------
+//  - iteration t: wait for tile t, barrier, request tile t + kAhead, values of
+//    tile t-1 (its P^T written in iteration t-1, double-buffered by tile
+//    parity), scores and softmax of tile t, P^T of tile t to LDS;
+//  - the ring keeps features 0..511 of kAhead + 2 tiles (t-1 for values, t for
+//    scores, kAhead in flight) and the rope features 512..575 of kAhead + 1;
+//    bf16 tiles (36 KB) allow 2 tiles in flight in the 160 KB of LDS, raw fp8
+//    tiles (18 KB) 3;
+//  - the slot list is not staged whole: a ring of 8 tiles' entries is refilled
+//    by an HBM->LDS copy of tile u + kAhead + 1's entries riding with the
+//    gathers of tile u, so the wait for tile u covers it and its barrier
+//    publishes it before tile u + kAhead + 1's gathers are issued;
+//  - the output scale 1/l of each head is handed from its score wave to the
+//    value waves through LDS after the last tile.
+template <bool FP8>
+struct AttnLayout {
+  static constexpr int kRowBytes = FP8 ? kRowB8 : kRowB;    // 576 or 1152
+  static constexpr int kBlocks = kRowBytes * kTile / 1024;  // 18 or 36 blocks of 1 KB
+  static constexpr int kMainBlocks = kBlocks * 8 / 9;       // features 0..511: 16 or 32
+  static constexpr int kMainB = kMainBlocks * 1024;
+  static constexpr int kRopeB = (kBlocks - kMainBlocks) * 1024;
+  static constexpr int kAhead = FP8 ? 3 : 2;                 // tiles in flight
+  static constexpr int kMainStages = kAhead + 2;
+  static constexpr int kRopeStages = kAhead + 1;
+  static constexpr int kRingB = kMainStages * kMainB + kRopeStages * kRopeB;
+  static constexpr int kStageB = kHPB * kEpiRow;             // epilogue staging
+  static constexpr int kTilesB = kRingB > kStageB ? kRingB : kStageB;
+  static constexpr int kDmaMax = (kBlocks + kAttnWaves - 1) / kAttnWaves;
+  static constexpr int kRefill = kAhead + 1;                 // slot refill distance in tiles
+  static constexpr int kKAhead = FP8 ? 3 : 2;                // key k-steps read ahead
+};
+constexpr int kPB = kTile * kHPB * 2;           // P^T of one tile, 128 heads (8 KB)
+constexpr int kSlotRing = 8;                    // tiles of slot entries held in LDS
+constexpr int kSlotInit = 4;                    // tiles whose entries are loaded at startup
+constexpr int kRefillWave = 7;                  // one of the waves with the fewest gathers
+constexpr int kFBW = kValue / 16 / kAttnWaves;  // 4 output feature blocks per wave
+constexpr int kNHB = kHPB / 16;                 // 8 head blocks
+static_assert(AttnLayout<false>::kBlocks == 36 && AttnLayout<false>::kMainBlocks == 32, "bf16");
+static_assert(AttnLayout<true>::kBlocks == 18 && AttnLayout<true>::kMainBlocks == 16, "fp8");
+static_assert(kSlotRing >= 2 * AttnLayout<true>::kAhead + 2 &&
+              kSlotRing >= 2 * AttnLayout<false>::kAhead + 2, "slot ring holds t .. t+2*ahead+1");
+static_assert(kSlotInit >= AttnLayout<true>::kRefill && kSlotInit >= AttnLayout<false>::kRefill,
+              "tiles before the first refill are loaded at startup");
+static_assert(AttnLayout<false>::kTilesB + 2 * kPB + kSlotRing * kTile * 4 + kHPB * 4 + 8 <=
+                  160 * 1024, "LDS budget");
+
+// fp32 pair -> packed bf16 (lo in the low half) by the hardware converter,
+// round to nearest even: one instruction, where the bit-level form takes a
+// dozen with a NaN branch and, unrolled over the epilogue, kilobytes of code
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// the lane index, recomputed where it is used: values derived from it are
+// then rebuilt in two instructions instead of being held across the tile loop
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 template <bool FP8, bool OFF32>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
     const float* __restrict__ cache_scale, int64_t num_slots, const int* __restrict__ slots,
     const int* __restrict__ counts, int k, int splits, float sm_scale,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kRingB = FP8 ? kTileB8 : kTileB;
-  constexpr int kDmaTotal = FP8 ? kDmaFp8Total : kDmaBf16Total;
-  constexpr int kDmaMax = (kDmaTotal + kAttnWaves - 1) / kAttnWaves;
-  constexpr int kMainB = kStages * kRingB;
-  constexpr int kSmemB = kMainB > kEpiB ? kMainB : kEpiB;
-  __shared__ __attribute__((aligned(16))) uint8_t s_main[kSmemB];
-  __shared__ int s_slot[kMaxSel];
-  __shared__ int s_restart[2];   // restart requests raised at tiles of each parity
-  uint8_t (*s_ring)[kRingB] = reinterpret_cast<uint8_t (*)[kRingB]>(s_main);
+  using Lay = AttnLayout<FP8>;
+  constexpr int kDmaMax = Lay::kDmaMax;
+  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[Lay::kTilesB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kPB];
+  __shared__ __attribute__((aligned(16))) int s_sring[kSlotRing * kTile];
+  __shared__ float s_inv[kHPB];
+  __shared__ int s_restart[2];
 
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin in launch
   // order, so the G = gridDim.y * gridDim.z workgroups of a row (its parts,
@@ -216,97 +287,64 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int g4 = lane >> 4;       // k-group of the 16x16x32 operands
   const int h0 = hg * kHPB + wave * kHPW;
   const int head = h0 + n16;
-  const bool wave_on = h0 < heads;
-  const bool head_on = head < heads;
+  const bool wave_on = h0 < heads;   // heads is a multiple of 16
+  const int n_hb = (heads - hg * kHPB) / 16 < kNHB ? (heads - hg * kHPB) / 16 : kNHB;
   const int out_part = yz % gridDim.y;
+  const int slot_lim = num_slots > 0x7fffffffLL ? 0x7fffffff : (int)num_slots;
 
-  // ---- startup loads: slot list, q, count ------------------------------------
-  // q fragments (B operand of S^T = K Q^T): head `head`, features 32*kk + 8*g4
-  // .. +8.  heads is a multiple of 16, so a wave's heads are all present or
-  // all absent; an absent wave loads head 0 (in bounds) and never uses it.
-  // Two load orders, chosen per cache type by measurement (the tile loop is
-  // the same code in both):
-  //  - bf16: the part's slot list (with one split it starts at position 0)
-  //    is requested together with the count instead of after it, all of a
-  //    thread's loads in flight at once, then q;
-  //  - fp8: count, then the list, then q, whose fragments are zeroed for
-  //    absent heads (the bf16 order measured ~7% slower here).
+  // ---- startup: count and the first tiles' slot entries ------------------------
   const int* my_slots = slots + ((int64_t)part * rows + row) * k;
-  const uint16_t* qp = q + ((int64_t)row * heads + (head_on ? head : 0)) * kLatent + 8 * g4;
-  constexpr int kSlotLd = kMaxSel / kAttnThreads;
-  int sl[kSlotLd];
-  bf16x8_t qf[kQSteps];
-  if constexpr (!FP8) {
-    if (splits == 1) {
-#pragma unroll
-      for (int j = 0; j < kSlotLd; ++j) {
-        const int i = tid + j * kAttnThreads;
-        sl[j] = i < k ? my_slots[i] : -1;
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
-  }
-
-  // this split's slice of the part's token list
   int cnt = counts ? counts[(int64_t)part * rows + row] : k;
+  bf16x8_t qf[kQSteps];   // loaded after the first gathers are issued
+  int sl0 = 0;
+  if (splits == 1 && tid < kSlotInit * kTile) sl0 = my_slots[tid];   // k >= 512
   cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
   if (num_slots <= 0) cnt = 0;
+  // this split's slice of the part's token list
   const int per = ((cnt + splits - 1) / splits + kTile - 1) / kTile * kTile;
   const int t_lo = split * per < cnt ? split * per : cnt;
   const int t_hi = t_lo + per < cnt ? t_lo + per : cnt;
   const int n_tok = t_hi - t_lo;
   const int ntiles = (n_tok + kTile - 1) / kTile;
+  auto load_first_slots = [&](bool have) {
+    if (tid < kSlotInit * kTile) {
+      int s = sl0;
+      if (!have) {
+        const int i = t_lo + tid;
+        s = my_slots[i < k ? i : k - 1];
+      }
+      s_sring[tid] = s;
+    }
+  };
+  load_first_slots(splits == 1);
 
-  if (!FP8 && splits == 1) {
+  f32x4_t o[kFBW][kNHB];
 #pragma unroll
-    for (int j = 0; j < kSlotLd; ++j) {
-      const int i = tid + j * kAttnThreads;
-      if (i < k) s_slot[i] = (sl[j] < 0 || (int64_t)sl[j] >= num_slots) ? -1 : sl[j];
-    }
-  } else {
-    for (int i = tid; i < n_tok; i += kAttnThreads) {
-      const int s = my_slots[t_lo + i];
-      s_slot[i] = (s < 0 || (int64_t)s >= num_slots) ? -1 : s;
-    }
-  }
-
+  for (int f = 0; f < kFBW; ++f)
+#pragma unroll
+    for (int hb = 0; hb < kNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float kv_scale = FP8 ? cache_scale[0] : 1.0f;
   const float qk_scale = sm_scale * kv_scale * kLog2e;
-  if constexpr (FP8) {
-#pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) {
-      u16x8_t v = *reinterpret_cast<const u16x8_t*>(qp + 32 * kk);
-      if (!head_on) v = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-  f32x4_t o[kOBlocks];
-#pragma unroll
-  for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
   if (tid < 2) s_restart[tid] = 0;
   lgkm_wait0();
-  bar();   // slot list and flag ready (q may still be in flight)
+  bar();   // first slot entries and flags ready
 
-  // ---- lane-invariant LDS byte offsets inside a bf16 tile -------------------
-  // scores: k-step kk, token block b reads block 2*kk + b at lane * 16.
-  // values (transpose reads): in 16-lane group g4, source lane s = n16 reads
-  // token 16*rd + 4*g4 + s/4 at features 16*fb + 4*(s%4): logical chunk
-  // 2fb + (s%4)/2, half s%2, so the offset is pv_base + 2048*(fb/2) +
-  // 512*(fb%2) + 1024*rd
+  // ---- lane-invariant LDS byte offsets ----------------------------------------
+  // bf16 tile: block (c/4)*2 + t/16 holds tokens 16*(t/16) .. +16 x 16-byte
+  // chunks 4*(c/4) .. +4 (32 features), token t, chunk c in slot (t % 16) +
+  // 16 * (c % 4).  A score k-step kk reads blocks 2kk and 2kk+1 at lane * 16.
+  // Value transpose reads: in 16-lane group g4, source lane s = n16 reads
+  // token 16*rd + 4*g4 + s/4 at features 16*fb + 4*(s%4): logical chunk 2fb +
+  // (s%4)/2, half s%2, at pv_base + 2048*(fb/2) + 512*(fb%2) + 1024*rd.
   const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
-  // ---- the same inside a raw fp8 tile --------------------------------------
-  // The raw tile keeps the block structure of the bf16 one with 16-code
-  // chunks: block 2*(c/4) + t/16 holds tokens 16*(t/16) .. +16 x chunks
-  // 4*(c/4) .. +4, and token t sits in slot ((t % 16) ^ (8 * (t/16))) +
-  // 16 * (c % 4) (the xor keeps the two token halves that one transpose read
-  // touches on different banks).
+  // raw fp8 tile: the same block structure with 16-code chunks (64 features
+  // per block), token t in slot ((t % 16) ^ (8 * (t/16))) + 16 * (c % 4) (the
+  // xor keeps the two token halves that one transpose read touches on
+  // different banks).
   //  - scores, k-step kk (chunks 2kk, 2kk+1), token block b: lane (n16, g4)
   //    reads the 8 codes of features 32kk + 8*g4 .. +8 of token 16b + n16 at
-  //    qk8_base[b] + 2048*(kk/2) + 512*(kk%2): each 32-lane half of the wave
-  //    reads 256 contiguous bytes;
+  //    qk8_base[b] + 2048*(kk/2) + 512*(kk%2);
   //  - values, block fb (chunk fb): ds_read_b64_tr_b8 hands lane i of a
   //    16-lane group byte i%8 of the 8-byte chunk addressed by lane 2e + i/8
   //    of its group as element e, so lane (s, g4) addresses half s%2 of the
@@ -319,95 +357,178 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int pv8_base = 1024 * (pv8_e >> 2) + 16 * ((4 * g4 + (pv8_e & 3)) ^ (8 * (pv8_e >> 2))) +
                        8 * (n16 & 1);
 
-  // ---- DMA issue of tile tt into its ring stage -------------------------------
-  // instruction `ins` fills 64 consecutive 16-byte chunk slots of the stage;
-  // instructions are dealt round-robin to the waves.  With OFF32 the source is
-  // the uniform cache base plus a 32-bit byte offset (one VGPR per lane).
-  // instruction ins fills block ins: tokens 16*(ins%2) + lane%16, 16-byte
-  // chunks 4*(ins/2) + lane/16 (bf16: 8 features; raw fp8: 16 features; fp8
-  // stores token half 1 with the slot xor described above).  With fp8 tiles
-  // the slot entries of the next gathers are read one tile ahead, right after
-  // the barrier, so that the issue itself waits on nothing; with bf16 tiles
-  // they are read just before the issue (measured: the read-ahead is ~3%
-  // faster for fp8 and ~5% slower for bf16).
-  auto tile_slots = [&](int tt, int (&sv)[kDmaMax]) {
-    const int tbase = tt * kTile;
+  auto main_stage = [&](int tt) { return s_tiles + (tt % Lay::kMainStages) * Lay::kMainB; };
+  auto rope_stage = [&](int tt) {
+    return s_tiles + Lay::kMainStages * Lay::kMainB + (tt % Lay::kRopeStages) * Lay::kRopeB;
+  };
+  // this wave's vector-memory operations for tile u: its gathers, and for the
+  // refill wave the copy of tile u + kRefill's slot entries
+  const int my_dma = Lay::kBlocks / kAttnWaves + (wave < Lay::kBlocks % kAttnWaves ? 1 : 0);
+  auto refills = [&](int u) {
+    return wave == kRefillWave && u + Lay::kRefill >= kSlotInit && u + Lay::kRefill < ntiles;
+  };
+  // gather instruction ins fills block ins: tokens 16*(ins%2) + lane%16
+  // (fp8: xor 8 on the second half), 16-byte chunks 4*(ins/2) + lane/16
+  auto tile_slots = [&](int u, int (&sv)[kDmaMax]) {
 #pragma unroll
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
       sv[jj] = 0;
-      if (ins < kDmaTotal) {
+      if (ins < Lay::kBlocks) {
         const int t = 16 * (ins & 1) + ((lane & 15) ^ (FP8 ? 8 * (ins & 1) : 0));
-        const int ti = tbase + t < n_tok ? tbase + t : 0;
-        sv[jj] = s_slot[ti];
+        sv[jj] = s_sring[(u % kSlotRing) * kTile + t];
       }
     }
   };
-  auto issue = [&](int tt, const int (&sv)[kDmaMax]) {
-    uint8_t* stage = s_ring[tt % kStages];
+  auto issue = [&](int u, const int (&sv)[kDmaMax]) {
+    if (refills(u) && lane < kTile) {
+      const int v = u + Lay::kRefill;
+      const int i = t_lo + v * kTile + lane_now();
+      __builtin_amdgcn_global_load_lds((const void*)(my_slots + (i < k ? i : k - 1)),
+                                       (lds_void_ptr)(s_sring + (v % kSlotRing) * kTile), 4, 0, 0);
+    }
+    uint8_t* ms = main_stage(u);
+    uint8_t* rs = rope_stage(u);
 #pragma unroll
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
-      if (ins < kDmaTotal) {
+      if (ins < Lay::kBlocks) {
         const int off = (4 * (ins >> 1) + (lane >> 4)) * 16;
-        const int s = max(sv[jj], 0);
+        const int s = (unsigned)sv[jj] < (unsigned)slot_lim ? sv[jj] : 0;
         const uint8_t* src;
         if constexpr (OFF32)
-          src = cache + (uint32_t)((uint32_t)s * (uint32_t)(FP8 ? kRowB8 : kRowB) + (uint32_t)off);
+          src = cache + (uint32_t)((uint32_t)s * (uint32_t)Lay::kRowBytes + (uint32_t)off);
         else
-          src = cache + (int64_t)s * (FP8 ? kRowB8 : kRowB) + off;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (lds_void_ptr)(stage + ins * kWave * 16), 16, 0, 0);
+          src = cache + (int64_t)s * Lay::kRowBytes + off;
+        uint8_t* dst = ins < Lay::kMainBlocks ? ms + ins * 1024 : rs + (ins - Lay::kMainBlocks) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)dst, 16, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // this wave's DMA instructions per tile
-  const int my_dma = kDmaTotal / kAttnWaves + (wave < kDmaTotal % kAttnWaves ? 1 : 0);
 
-  // ---- one tile, first half: scores -------------------------------------------
-  // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
+  // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1); the key operands
+  // are read kKAhead k-steps ahead of their products
   auto scores = [&](int tt, f32x4_t& s0, f32x4_t& s1) {
-    const uint8_t* tile = s_ring[tt % kStages];
     s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (!wave_on) return;
+    constexpr int A = Lay::kKAhead;
     if constexpr (FP8) {
-#pragma unroll
-      for (int kk = 0; kk < kQSteps; ++kk) {
-        const int ko = 2048 * (kk >> 1) + 512 * (kk & 1);
-        const uint2 r0 = *reinterpret_cast<const uint2*>(tile + qk8_base0 + ko);
-        const uint2 r1 = *reinterpret_cast<const uint2*>(tile + qk8_base1 + ko);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(r0.x, r0.y), qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(r1.x, r1.y), qf[kk], s1, 0, 0, 0);
-      }
+      const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + qk8_base0);
+      const uint32_t m1 = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + qk8_base1);
+      const uint32_t r0 = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + qk8_base0);
+      const uint32_t r1 = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + qk8_base1);
+      i32x2_t ka[kQSteps], kb[kQSteps];
+      auto rd = [&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        if constexpr (kk < 16) {
+          ka[kk] = lds_read_b64<2048 * (kk >> 1) + 512 * (kk & 1)>(m0);
+          kb[kk] = lds_read_b64<2048 * (kk >> 1) + 512 * (kk & 1)>(m1);
+        } else {
+          ka[kk] = lds_read_b64<512 * (kk & 1)>(r0);
+          kb[kk] = lds_read_b64<512 * (kk & 1)>(r1);
+        }
+      };
+      static_for<A>([&](auto kc) { rd(kc); });
+      static_for<kQSteps>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        constexpr int last = kk + A - 1 < kQSteps - 1 ? kk + A - 1 : kQSteps - 1;
+        lgkm_wait_2v<2 * (last - kk)>(ka[kk], kb[kk]);
+        if constexpr (kk + A < kQSteps) rd(IntC<kk + A>{});
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(ka[kk].x, ka[kk].y), qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kb[kk].x, kb[kk].y), qf[kk], s1, 0, 0, 0);
+      });
     } else {
+      const uint32_t ma = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 16 * lane);
+      const uint32_t ra = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + 16 * lane);
+      u32x4_t ka[kQSteps], kb[kQSteps];
+      auto rd = [&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        if constexpr (kk < 16) {
+          ka[kk] = lds_read_b128<2048 * kk>(ma);
+          kb[kk] = lds_read_b128<2048 * kk + 1024>(ma);
+        } else {
+          ka[kk] = lds_read_b128<2048 * (kk - 16)>(ra);
+          kb[kk] = lds_read_b128<2048 * (kk - 16) + 1024>(ra);
+        }
+      };
+      static_for<A>([&](auto kc) { rd(kc); });
+      static_for<kQSteps>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        constexpr int last = kk + A - 1 < kQSteps - 1 ? kk + A - 1 : kQSteps - 1;
+        lgkm_wait_2<2 * (last - kk)>(ka[kk], kb[kk]);
+        if constexpr (kk + A < kQSteps) rd(IntC<kk + A>{});
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[kk]), qf[kk],
+                                                     s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[kk]), qf[kk],
+                                                     s1, 0, 0, 0);
+      });
+    }
+  };
+  // O^T += V^T P^T for this wave's 4 feature blocks and every present head
+  // block; the P^T of head block hb is what lane `lane` of score wave hb wrote
+  auto values = [&](int tt) {
+    const uint8_t* pb = s_p[tt & 1] + 16 * lane;
+    bf16x8_t va[kFBW];
+    if constexpr (FP8) {
+      // features 16*(4*wave + f) + lane%16, 8 tokens in the P^T order
+      const uint32_t vb =
+          (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv8_base + 2048 * wave);
+      i32x2_t r[kFBW];
+      static_for<kFBW>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        r[f] = lds_read_tr8<256 * f>(vb);
+      });
+      lgkm_wait_4v<0>(r[0], r[1], r[2], r[3]);
 #pragma unroll
-      for (int kk = 0; kk < kQSteps; ++kk) {
-        const uint8_t* a = tile + 2048 * kk + 16 * lane;
-        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a);
-        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a + 1024);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[kk], s1, 0, 0, 0);
+      for (int f = 0; f < kFBW; ++f) va[f] = widen8((uint32_t)r[f].x, (uint32_t)r[f].y);
+    } else {
+      // ds_read_b64_tr_b16 of features 16*(4*wave + f) + lane%16 for tokens
+      // 4*g4 + e (first read) and 16 + 4*g4 + e (second)
+      const uint32_t vb =
+          (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv_base + 4096 * wave);
+      i32x2_t r[2 * kFBW];
+      static_for<kFBW>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        r[2 * f] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1)>(vb);
+        r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1) + 1024>(vb);
+      });
+      lgkm_wait_4v<0>(r[0], r[1], r[2], r[3]);
+      lgkm_wait_4v<0>(r[4], r[5], r[6], r[7]);
+#pragma unroll
+      for (int f = 0; f < kFBW; ++f)
+        va[f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2, 3));
+    }
+    bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pb);
+#pragma unroll
+    for (int hb = 0; hb < kNHB; ++hb) {
+      if (hb < n_hb) {
+        bf16x8_t pn = pa;
+        if (hb + 1 < n_hb) pn = *reinterpret_cast<const bf16x8_t*>(pb + 1024 * (hb + 1));
+#pragma unroll
+        for (int f = 0; f < kFBW; ++f)
+          o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
+        pa = pn;
       }
     }
   };
-
-  // ---- one tile, second half: mask, softmax, values ----------------------------
-  // sv: the slot entry of token lane % 32 of the tile, read without a bound
-  // (the list has room for every tile); tokens past the tile's end are masked
-  // by position
+  // mask, softmax against the reference max, P^T of tile tt to LDS.  sv: the
+  // slot entry of token lane % 32 of the tile; tokens past the tile's end are
+  // masked by position
   auto finish = [&](int tt, int sv, f32x4_t s0, f32x4_t s1) {
-    const uint8_t* tile = s_ring[tt % kStages];
     const int tbase = tt * kTile;
-    const uint32_t vmask = (uint32_t)__ballot(lane < kTile && tbase + lane < n_tok && sv >= 0);
+    const int ln = lane_now();
+    const uint32_t vmask = (uint32_t)__ballot(ln < kTile && tbase + ln < n_tok &&
+                                              (unsigned)sv < (unsigned)slot_lim);
     if (!wave_on) return;
     // lane holds head `head`, tokens 4*g4 + i (s0) and 16 + 4*g4 + i (s1)
     if (vmask != 0xffffffffu) {
+      const uint32_t mv = vmask >> (4 * (lane_now() >> 4));   // bit i: token 4*g4 + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (!((vmask >> (4 * g4 + i)) & 1u)) s0[i] = -INFINITY;
-        if (!((vmask >> (16 + 4 * g4 + i)) & 1u)) s1[i] = -INFINITY;
+        s0[i] = (mv >> i) & 1u ? s0[i] : -INFINITY;
+        s1[i] = (mv >> (16 + i)) & 1u ? s1[i] : -INFINITY;
       }
     }
     float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
@@ -431,415 +552,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     }
     const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
     // P^T operand: element e < 4 is token 4*g4 + e, element 4 + e is token
-    // 16 + 4*g4 + e (the value fragments below use the same token order)
-    bf16x8_t pf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], qk_scale, nm));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], qk_scale, nm));
-      l_part += p0;
-      l_part += p1;
-      pf[i] = static_cast<__bf16>(p0);
-      pf[4 + i] = static_cast<__bf16>(p1);
-    }
-    // O^T += V^T P^T, 16 output features per block: ds_read_b64_tr_b16 gives
-    // lane (g4, n16) element e = V[token 4*g4 + e (+16)][16*fb + n16]
-    if constexpr (FP8) {
-      // raw codes of the next block in flight while the current one is
-      // widened and multiplied
-      const uint32_t pv8 = (uint32_t)(uintptr_t)(lds_void_ptr)(tile + pv8_base);
-      i32x2_t r[kOBlocks];
-      r[0] = lds_read_tr8<0>(pv8);
-      static_for<kOBlocks>([&](auto fbc) {
-        constexpr int fb = decltype(fbc)::value;
-        if constexpr (fb + 1 < kOBlocks) {
-          r[fb + 1] = lds_read_tr8<2048 * ((fb + 1) >> 2) + 256 * ((fb + 1) & 3)>(pv8);
-          lgkm_wait_v<1>(r[fb]);
-        } else {
-          lgkm_wait_v<0>(r[fb]);
-        }
-        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            widen8((uint32_t)r[fb].x, (uint32_t)r[fb].y), pf, o[fb], 0, 0, 0);
-        if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-      });
-    } else {
-      auto vfrag = [&](int fb) {
-        const uint8_t* b = tile + pv_base + 2048 * (fb >> 1) + 512 * (fb & 1);
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b));
-        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(b + 1024));
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8_t va = vfrag(0);
-#pragma unroll
-      for (int fb = 0; fb < kOBlocks; ++fb) {
-        bf16x8_t nb = va;
-        if (fb + 1 < kOBlocks) nb = vfrag(fb + 1);   // next block's fragment in flight
-        o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[fb], 0, 0, 0);
-        if (fb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-        va = nb;
-      }
-    }
-  };
-
-  // Iteration tt requests tiles up to tt+2 (tile tt+2 goes to the stage of
-  // tile tt-2, which every wave left before the previous barrier), waits for
-  // tile tt, passes the barrier (every wave is then done with tile tt-1) and
-  // computes tile tt.  A restart request raised while computing tile tt goes
-  // to flag slot tt % 2 and is read after the next barrier: inside the loop
-  // at the next tile's barrier, after the last tile at the barrier below the
-  // loop.  With two slots, a fast wave raising a request at tile tt never
-  // writes the slot a slower wave may still be reading for tile tt-1.
-  int tt = 0;
-  int next_issue = 0;
-  int nsv[kDmaMax];      // slot entries of tile next_issue when `ahead`
-  bool ahead = false;
-  for (;;) {
-  for (; tt < ntiles;) {
-    while (next_issue < ntiles && next_issue <= tt + 2) {
-      if (!ahead) tile_slots(next_issue, nsv);
-      issue(next_issue++, nsv);
-      ahead = false;
-    }
-    vm_wait_n(my_dma * (next_issue - 1 - tt));
-    lgkm_wait0();
-    bar();   // tile tt visible; every wave is done with tile tt-1
-    // the restart flag raised at tile tt-1 (slot 1 is clear at tt = 0) and the
-    // tile's slot entries are requested here and first used after the score
-    // products, which change nothing that a restart keeps
-    const int rflag = s_restart[(tt + 1) & 1];
-    const int sv = s_slot[tt * kTile + (lane & 31)];
-    if (FP8 && next_issue < ntiles) {   // next iteration's gathers
-      tile_slots(next_issue, nsv);
-      ahead = true;
-    }
-    f32x4_t s0, s1;
-    scores(tt, s0, s1);
-    if (__builtin_amdgcn_readfirstlane(rflag)) {
-      // a reference max moved by more than 2^64: drop the partial sums and
-      // replay the token list (every wave, since the tile ring is shared)
-      vm_wait<0>();
-      bar();
-      if (tid < 2) s_restart[tid] = 0;
-#pragma unroll
-      for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      l_part = 0.f;
-      __syncthreads();
-      tt = 0;
-      next_issue = 0;
-      ahead = false;
-      continue;
-    }
-    finish(tt, sv, s0, s1);
-    ++tt;
-  }
-  lgkm_wait0();
-  bar();
-  if (!s_restart[(tt + 1) & 1]) break;   // raised at the last tile, ntiles - 1
-  bar();
-  if (tid < 2) s_restart[tid] = 0;
-#pragma unroll
-  for (int fb = 0; fb < kOBlocks; ++fb) o[fb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  l_part = 0.f;
-  __syncthreads();
-  tt = 0;
-  next_issue = 0;
-  ahead = false;
-  }
-
-  // ---- epilogue ---------------------------------------------------------------
-  // Each wave stages its 16 heads x 512 normalised bf16 outputs row-major in
-  // LDS (the ring is free: every wave passed the barrier after the last tile),
-  // then stores one whole 1 KB head row per instruction.
-  float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
-  const float inv = l_tot > 0.f ? kv_scale / l_tot : 0.f;
-  uint8_t* stg = s_main + wave * kEpiWaveB;
-  if (wave_on) {
-#pragma unroll
-    for (int fb = 0; fb < kOBlocks; ++fb) {
-      const uint2 v = make_uint2(pack_bf16x2(o[fb][0] * inv, o[fb][1] * inv),
-                                 pack_bf16x2(o[fb][2] * inv, o[fb][3] * inv));
-      *reinterpret_cast<uint2*>(stg + n16 * kEpiRow + (16 * fb + 4 * g4) * 2) = v;
-    }
-  }
-  lgkm_wait0();   // a wave reads back only what it wrote itself
-  if (wave_on) {
-    uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue;
-#pragma unroll
-    for (int r = 0; r < kHPW; ++r) {
-      if (h0 + r < heads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kEpiRow + lane * 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + lane * 16) = v;
-      }
-    }
-    if (head_on && g4 == 0) {
-      const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-      lse[((int64_t)out_part * rows + row) * heads + head] = lv;
-    }
-  }
-}
-
-// ---- bf16 caches: the waves share the probabilities through LDS ---------------
-// Score phase as above (a wave: 16 heads x all 576 features, q in registers).
-// Value phase split by output features instead of heads: wave w owns features
-// 64w .. 64w+63 for all 128 heads, so it reads 4 value fragments per tile
-// instead of 32 and takes the 8 heads blocks' P^T operands (1 KB each) that
-// the score waves wrote to LDS.  The LDS bytes a tile costs drop from
-// 8 x (36 + 32) KB to 8 x (36 + 4 + 8) + 8 KB.  Pipelining:
-//  - iteration t: wait for tile t, barrier, request tile t+2, values of tile
-//    t-1 (its P^T written in iteration t-1, double-buffered by tile parity),
-//    scores and softmax of tile t, P^T of tile t to LDS;
-//  - the ring keeps features 0..511 of 4 tiles (t-1 for values, t for scores,
-//    t+1 and t+2 in flight) and features 512..575 of 3 (t, t+1, t+2);
-//  - the slot list is not staged whole: a ring of 8 tiles' entries is refilled
-//    by an HBM->LDS copy that rides with the gathers of the tile 3 earlier, so
-//    the wait for that tile covers it and its barrier publishes it.
-// The output scale 1/l of each head is handed from its score wave to the
-// value waves through LDS after the last tile.
-constexpr int kSpMainB = 32 * 1024;             // features 0..511 of a tile
-constexpr int kSpRopeB = 4 * 1024;              // features 512..575
-constexpr int kSpMainStages = 4;
-constexpr int kSpRopeStages = 3;
-constexpr int kSpTilesB = kSpMainStages * kSpMainB + kSpRopeStages * kSpRopeB;
-constexpr int kSpPB = kTile * kHPB * 2;         // P^T of one tile, 128 heads (8 KB)
-constexpr int kSpSlotRing = 8;                  // tiles of slot entries held in LDS
-constexpr int kSpSlotInit = 4;                  // tiles whose entries are loaded at startup
-constexpr int kSpRefillWave = 7;                // has 4 gathers per tile, the others 4 or 5
-constexpr int kSpFBW = kValue / 16 / kAttnWaves;   // 4 output feature blocks per wave
-constexpr int kSpNHB = kHPB / 16;                  // 8 head blocks
-static_assert(kHPB * kEpiRow <= kSpTilesB, "epilogue staging fits in the tile ring");
-static_assert(kDmaBf16Total == 36 && kSpMainB / 1024 == 32, "32 main + 4 rope blocks per tile");
-
-// the lane index, recomputed where it is used: values derived from it are
-// then rebuilt in two instructions instead of being held across the tile loop
-__device__ __forceinline__ int lane_now() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
-template <bool OFF32>
-__global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
-    const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
-    int64_t num_slots, const int* __restrict__ slots, const int* __restrict__ counts, int k,
-    int splits, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kDmaMax = (kDmaBf16Total + kAttnWaves - 1) / kAttnWaves;   // 5
-  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kSpTilesB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kSpPB];
-  __shared__ __attribute__((aligned(16))) int s_sring[kSpSlotRing * kTile];
-  __shared__ float s_inv[kHPB];
-  __shared__ int s_restart[2];
-
-  int row, yz;   // XCD-aware order, as in the kernel above
-  {
-    const int G = gridDim.y * gridDim.z;
-    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int b = L / (8 * G), w = L % (8 * G);
-    const int nr = rows - 8 * b < 8 ? rows - 8 * b : 8;
-    row = 8 * b + w % nr;
-    yz = w / nr;
-  }
-  const int part = (yz % gridDim.y) / splits;
-  const int split = (yz % gridDim.y) % splits;
-  const int hg = yz / gridDim.y;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = lane_id();
-  const int n16 = lane & 15;
-  const int g4 = lane >> 4;
-  const int h0 = hg * kHPB + wave * kHPW;
-  const int head = h0 + n16;
-  const bool wave_on = h0 < heads;   // heads is a multiple of 16
-  const int n_hb = (heads - hg * kHPB) / 16 < kSpNHB ? (heads - hg * kHPB) / 16 : kSpNHB;
-  const int out_part = yz % gridDim.y;
-  const int slot_lim = num_slots > 0x7fffffffLL ? 0x7fffffff : (int)num_slots;
-
-  // ---- startup: count, the first tiles' slot entries, q -------------------------
-  const int* my_slots = slots + ((int64_t)part * rows + row) * k;
-  int cnt = counts ? counts[(int64_t)part * rows + row] : k;
-  bf16x8_t qf[kQSteps];   // loaded after the first gathers are issued
-  int sl0 = 0;
-  if (splits == 1 && tid < kSpSlotInit * kTile) sl0 = my_slots[tid];   // k >= 512
-  cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
-  if (num_slots <= 0) cnt = 0;
-  const int per = ((cnt + splits - 1) / splits + kTile - 1) / kTile * kTile;
-  const int t_lo = split * per < cnt ? split * per : cnt;
-  const int t_hi = t_lo + per < cnt ? t_lo + per : cnt;
-  const int n_tok = t_hi - t_lo;
-  const int ntiles = (n_tok + kTile - 1) / kTile;
-  auto load_first_slots = [&](bool have) {
-    if (tid < kSpSlotInit * kTile) {
-      int s = sl0;
-      if (!have) {
-        const int i = t_lo + tid;
-        s = my_slots[i < k ? i : k - 1];
-      }
-      s_sring[tid] = s;
-    }
-  };
-  load_first_slots(splits == 1);
-
-  f32x4_t o[kSpFBW][kSpNHB];
-#pragma unroll
-  for (int f = 0; f < kSpFBW; ++f)
-#pragma unroll
-    for (int hb = 0; hb < kSpNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float qk_scale = sm_scale * kLog2e;
-  float m_ref = -INFINITY, l_part = 0.f;
-  if (tid < 2) s_restart[tid] = 0;
-  lgkm_wait0();
-  bar();   // first slot entries and flags ready
-
-  const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
-  auto main_stage = [&](int tt) { return s_tiles + (tt & (kSpMainStages - 1)) * kSpMainB; };
-  auto rope_stage = [&](int tt) {
-    return s_tiles + kSpMainStages * kSpMainB + (tt % kSpRopeStages) * kSpRopeB;
-  };
-  // this wave's vector-memory operations for tile u: its gathers, and for the
-  // refill wave the copy of tile u+3's slot entries
-  const int my_dma = kDmaBf16Total / kAttnWaves + (wave < kDmaBf16Total % kAttnWaves ? 1 : 0);
-  auto refills = [&](int u) {
-    return wave == kSpRefillWave && u + 3 >= kSpSlotInit && u + 3 < ntiles;
-  };
-  auto tile_slots = [&](int u, int (&sv)[kDmaMax]) {
-#pragma unroll
-    for (int jj = 0; jj < kDmaMax; ++jj) {
-      const int ins = jj * kAttnWaves + wave;
-      sv[jj] = 0;
-      if (ins < kDmaBf16Total)
-        sv[jj] = s_sring[(u & (kSpSlotRing - 1)) * kTile + 16 * (ins & 1) + (lane & 15)];
-    }
-  };
-  // block ins of tile u: tokens 16*(ins%2) + lane%16, 16-byte chunks 4*(ins/2)
-  // + lane/16; blocks 0..31 go to the main stage, 32..35 to the rope stage
-  auto issue = [&](int u, const int (&sv)[kDmaMax]) {
-    if (refills(u) && lane < kTile) {
-      const int i = t_lo + (u + 3) * kTile + lane_now();
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(my_slots + (i < k ? i : k - 1)),
-          (lds_void_ptr)(s_sring + ((u + 3) & (kSpSlotRing - 1)) * kTile), 4, 0, 0);
-    }
-    uint8_t* ms = main_stage(u);
-    uint8_t* rs = rope_stage(u);
-#pragma unroll
-    for (int jj = 0; jj < kDmaMax; ++jj) {
-      const int ins = jj * kAttnWaves + wave;
-      if (ins < kDmaBf16Total) {
-        const int off = (4 * (ins >> 1) + (lane >> 4)) * 16;
-        const int s = (unsigned)sv[jj] < (unsigned)slot_lim ? sv[jj] : 0;
-        const uint8_t* src;
-        if constexpr (OFF32)
-          src = cache + (uint32_t)((uint32_t)s * (uint32_t)kRowB + (uint32_t)off);
-        else
-          src = cache + (int64_t)s * kRowB + off;
-        uint8_t* dst = ins < 32 ? ms + ins * 1024 : rs + (ins - 32) * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)dst, 16, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // S^T = K Q^T for token blocks 0..15 (s0) and 16..31 (s1)
-  // the key operands of k-step kk (token blocks 0..15 and 16..31) are read
-  // two k-steps ahead of their products
-  auto scores = [&](int tt, f32x4_t& s0, f32x4_t& s1) {
-    s0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (!wave_on) return;
-    const uint32_t ma = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 16 * lane);
-    const uint32_t ra = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + 16 * lane);
-    u32x4_t ka[kQSteps], kb[kQSteps];
-    auto rd = [&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
-      if constexpr (kk < 16) {
-        ka[kk] = lds_read_b128<2048 * kk>(ma);
-        kb[kk] = lds_read_b128<2048 * kk + 1024>(ma);
-      } else {
-        ka[kk] = lds_read_b128<2048 * (kk - 16)>(ra);
-        kb[kk] = lds_read_b128<2048 * (kk - 16) + 1024>(ra);
-      }
-    };
-    rd(IntC<0>{});
-    rd(IntC<1>{});
-    static_for<kQSteps>([&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
-      if constexpr (kk + 1 < kQSteps) lgkm_wait_2<2>(ka[kk], kb[kk]);
-      else lgkm_wait_2<0>(ka[kk], kb[kk]);
-      if constexpr (kk + 2 < kQSteps) rd(IntC<kk + 2>{});
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[kk]), qf[kk], s0,
-                                                   0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[kk]), qf[kk], s1,
-                                                   0, 0, 0);
-    });
-  };
-
-  // O^T += V^T P^T for this wave's 4 feature blocks and every present head
-  // block; the P^T of head block hb is what lane `lane` of score wave hb wrote
-  auto values = [&](int tt) {
-    const uint32_t vb =
-        (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv_base + 4096 * wave);
-    const uint8_t* pb = s_p[tt & 1] + 16 * lane;
-    // the 4 value fragments: ds_read_b64_tr_b16 of features 16*(4*wave + f) +
-    // lane%16 for tokens 4*g4 + e (first read) and 16 + 4*g4 + e (second)
-    i32x2_t r[2 * kSpFBW];
-    static_for<kSpFBW>([&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      r[2 * f] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1)>(vb);
-      r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1) + 1024>(vb);
-    });
-    bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pb);
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
-                   "+v"(r[6]), "+v"(r[7]));
-    bf16x8_t va[kSpFBW];
-#pragma unroll
-    for (int f = 0; f < kSpFBW; ++f)
-      va[f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2, 3));
-#pragma unroll
-    for (int hb = 0; hb < kSpNHB; ++hb) {
-      if (hb < n_hb) {
-        bf16x8_t pn = pa;
-        if (hb + 1 < n_hb) pn = *reinterpret_cast<const bf16x8_t*>(pb + 1024 * (hb + 1));
-#pragma unroll
-        for (int f = 0; f < kSpFBW; ++f)
-          o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
-        pa = pn;
-      }
-    }
-  };
-
-  // mask, softmax against the reference max, P^T of tile tt to LDS
-  auto finish = [&](int tt, int sv, f32x4_t s0, f32x4_t s1) {
-    const int tbase = tt * kTile;
-    const int ln = lane_now();
-    const uint32_t vmask = (uint32_t)__ballot(ln < kTile && tbase + ln < n_tok &&
-                                              (unsigned)sv < (unsigned)slot_lim);
-    if (!wave_on) return;
-    if (vmask != 0xffffffffu) {
-      const uint32_t mv = vmask >> (4 * (lane_now() >> 4));   // bit i: token 4*g4 + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s0[i] = (mv >> i) & 1u ? s0[i] : -INFINITY;
-        s1[i] = (mv >> (16 + i)) & 1u ? s1[i] : -INFINITY;
-      }
-    }
-    float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    {
-      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                      false, false);
-      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                      false, false);
-      mt = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])) * qk_scale;
-    }
-    if (m_ref == -INFINITY) {
-      m_ref = mt;
-    } else if (__any(mt > m_ref + kRestartSlack)) {
-      m_ref = fmaxf(m_ref, mt);
-      if (lane == 0) s_restart[tt & 1] = 1;
-    }
-    const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    // 16 + 4*g4 + e (the value fragments use the same token order)
     bf16x8_t pf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -853,23 +566,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
     *reinterpret_cast<bf16x8_t*>(s_p[tt & 1] + (wave * kWave + lane_now()) * 16) = pf;
   };
 
-  // both tiles' slot entries are read before the first gather is issued
+  // the first kAhead tiles' slot entries are all read before a gather is issued
   auto start = [&]() {
-    int sv0[kDmaMax], sv1[kDmaMax];
-    tile_slots(0, sv0);
-    tile_slots(1, sv1);
-    if (ntiles > 0) issue(0, sv0);
-    if (ntiles > 1) issue(1, sv1);
+    int sv[Lay::kAhead][kDmaMax];
+#pragma unroll
+    for (int u = 0; u < Lay::kAhead; ++u) tile_slots(u, sv[u]);
+#pragma unroll
+    for (int u = 0; u < Lay::kAhead; ++u)
+      if (u < ntiles) issue(u, sv[u]);
   };
   start();
-  // q (the B operand of the score products) is requested after the first two
-  // tiles' gathers, and everything in flight is waited for before the loop,
-  // so that inside it q is known to be in registers
+  // q is requested after the first tiles' gathers, and everything in flight
+  // is waited for before the loop, so that inside it q is plain registers
   const uint16_t* qp = q + ((int64_t)row * heads + (wave_on ? head : 0)) * kLatent + 8 * g4;
 #pragma unroll
   for (int kk = 0; kk < kQSteps; ++kk)
     qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
-  // the wait passes q through, so the loop sees q as plain registers
   asm volatile("s_waitcnt vmcnt(0)"
                : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
                  "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]),
@@ -879,18 +591,26 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
                : "memory");
   // A restart request raised while finishing tile t goes to flag slot t % 2
   // and is read after the next barrier, in iteration t+1 (the last tile's in
-  // the extra iteration t = ntiles, which only finishes the values).
+  // the extra iteration t = ntiles, which only finishes the values).  With two
+  // slots, a fast wave raising a request never writes the slot a slower wave
+  // may still be reading.
   for (int t = 0; t <= ntiles;) {
-    if (t + 1 < ntiles) vm_wait_n(my_dma + (refills(t + 1) ? 1 : 0));
-    else vm_wait<0>();
+    {   // wait for this wave's gathers of tile t: those of later tiles may fly
+      int after = 0;
+#pragma unroll
+      for (int d = 1; d < Lay::kAhead; ++d)
+        if (t + d < ntiles) after += my_dma + (refills(t + d) ? 1 : 0);
+      if (t < ntiles) vm_wait_n(after);
+      else vm_wait<0>();
+    }
     lgkm_wait0();
     bar();   // tile t visible; P^T of tile t-1 written; every wave done with tile t-2
-    const int rflag = s_restart[(t + 1) & 1];
-    const int sv = t < ntiles ? s_sring[(t & (kSpSlotRing - 1)) * kTile + (lane & 31)] : 0;
-    if (t + 2 < ntiles) {
+    const int rflag = s_restart[(t + 1) & 1];   // raised while finishing tile t-1
+    const int sv = t < ntiles ? s_sring[(t % kSlotRing) * kTile + (lane & 31)] : 0;
+    if (t + Lay::kAhead < ntiles) {
       int nsv[kDmaMax];
-      tile_slots(t + 2, nsv);
-      issue(t + 2, nsv);
+      tile_slots(t + Lay::kAhead, nsv);
+      issue(t + Lay::kAhead, nsv);
     }
     if (t >= 1) values(t - 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -904,9 +624,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
       bar();
       if (tid < 2) s_restart[tid] = 0;
 #pragma unroll
-      for (int f = 0; f < kSpFBW; ++f)
+      for (int f = 0; f < kFBW; ++f)
 #pragma unroll
-        for (int hb = 0; hb < kSpNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int hb = 0; hb < kNHB; ++hb) o[f][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_part = 0.f;
       load_first_slots(false);
       __syncthreads();
@@ -922,21 +642,23 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_bf16_kernel(
   float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
   if (wave_on && g4 == 0) {
-    s_inv[wave * kHPW + n16] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    s_inv[wave * kHPW + n16] = l_tot > 0.f ? kv_scale / l_tot : 0.f;
     const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     lse[((int64_t)out_part * rows + row) * heads + head] = lv;
   }
   lgkm_wait0();
   bar();   // 1/l of every head published; every wave done with the ring
+  // staging: head rows of 512 bf16 outputs, padded by 16 bytes so that the
+  // row-strided 8-byte writes spread over the banks
 #pragma unroll
-  for (int hb = 0; hb < kSpNHB; ++hb) {
+  for (int hb = 0; hb < kNHB; ++hb) {
     if (hb < n_hb) {
       const float inv = s_inv[16 * hb + n16];
       uint8_t* stg = s_tiles + (16 * hb + n16) * kEpiRow + (64 * wave + 4 * g4) * 2;
 #pragma unroll
-      for (int f = 0; f < kSpFBW; ++f) {
-        const uint2 v = make_uint2(pack_bf16x2(o[f][hb][0] * inv, o[f][hb][1] * inv),
-                                   pack_bf16x2(o[f][hb][2] * inv, o[f][hb][3] * inv));
+      for (int f = 0; f < kFBW; ++f) {
+        const uint2 v = make_uint2(cvt_pk_bf16(o[f][hb][0] * inv, o[f][hb][1] * inv),
+                                   cvt_pk_bf16(o[f][hb][2] * inv, o[f][hb][3] * inv));
         *reinterpret_cast<uint2*>(stg + 32 * f) = v;
       }
     }
@@ -971,14 +693,8 @@ int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cac
     if (off32) DSA_ATTN(true, true);
     else DSA_ATTN(true, false);
   } else {
-    if (off32)
-      hipLaunchKernelGGL((sparse_mla_decode_bf16_kernel<true>), grid, dim3(kAttnThreads), 0,
-                         stream, q16, rows, heads, c8, num_slots, slots, counts, k, splits,
-                         sm_scale, o16, lse);
-    else
-      hipLaunchKernelGGL((sparse_mla_decode_bf16_kernel<false>), grid, dim3(kAttnThreads), 0,
-                         stream, q16, rows, heads, c8, num_slots, slots, counts, k, splits,
-                         sm_scale, o16, lse);
+    if (off32) DSA_ATTN(false, true);
+    else DSA_ATTN(false, false);
   }
 #undef DSA_ATTN
   return 0;
