@@ -19,10 +19,19 @@ constexpr int kCombineThreads = 256;
 constexpr int kCombineFast = 8;   // partials held in registers at once
 constexpr float kLog2eC = 1.4426950408889634f;
 
+// acc += w * v for the 8 bf16 values of v; a zero weight (an empty partial,
+// or a slot past the partial count) adds nothing, whatever v holds
 __device__ __forceinline__ void accumulate8(float (&acc)[8], float w, const uint4 v) {
-  const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+  const bool on = w != 0.f;
+  const uint32_t ws[4] = {on ? v.x : 0u, on ? v.y : 0u, on ? v.z : 0u, on ? v.w : 0u};
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] += w * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+}
+// fp32 pair -> packed bf16 (lo in the low half), hardware round to nearest even
+__device__ __forceinline__ uint32_t cvt_pk_bf16c(float lo, float hi) {
+  typedef __bf16 bf16x2c_t __attribute__((ext_vector_type(2)));
+  const bf16x2c_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <bool FAST>
@@ -59,7 +68,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
       for (int p = 0; p < kCombineFast; ++p) {
         const float w = exp2f((l[p] - M) * kLog2eC);   // exp(-inf) = 0
         z += w;
-        if (w != 0.f) accumulate8(acc, w, v[p]);          // an empty partial adds nothing
+        accumulate8(acc, w, v[p]);
       }
     }
   } else {
@@ -82,16 +91,16 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           z += w[b];
-          if (w[b] != 0.f) accumulate8(acc, w[b], v[b]);
+          accumulate8(acc, w[b], v[b]);
         }
       }
     }
   }
   const float inv = z > 0.f ? 1.0f / z : 0.f;
-  const uint4 o = make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                             pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                             pack_bf16x2(acc[4] * inv, acc[5] * inv),
-                             pack_bf16x2(acc[6] * inv, acc[7] * inv));
+  const uint4 o = make_uint4(cvt_pk_bf16c(acc[0] * inv, acc[1] * inv),
+                             cvt_pk_bf16c(acc[2] * inv, acc[3] * inv),
+                             cvt_pk_bf16c(acc[4] * inv, acc[5] * inv),
+                             cvt_pk_bf16c(acc[6] * inv, acc[7] * inv));
   *reinterpret_cast<uint4*>(out + rh * dim + c * 8) = o;
   if (lse_out && c == 0) lse_out[rh] = (M == -INFINITY) ? -INFINITY : M + logf(z);
 }
