@@ -92,13 +92,11 @@ def topk_traffic(c, n_valid_logits, fused=True):
 
 def measured_traffic(workload):
     """HBM bytes per sparse_mla_decode launch from the committed counter
-    summary, or None when the summary is for another workload or the kernel
-    source changed since the counters were taken."""
+    summary of this workload, or None when there is none or the kernel source
+    changed since the counters were taken."""
     import hashlib
     import re
-    if workload != "decode":
-        return None
-    summary = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
+    summary = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
     src = os.path.join(ROOT, "sparse_attention_indexer_topk_amd", "csrc", "sparse_mla_decode.hip")
     try:
         text = open(summary).read()
