@@ -114,6 +114,9 @@ PARITY_CASES = {
     # block table; 2 shards, as in the pages' [4, 4, 5] localisation example
     "mtp_s": Spec("mtp_s", rows=9, ctx=9001, shards=2, interleave=1, k=512,
                   heads=16, seed=18, q_len=3),
+    # more heads than one workgroup holds: a full group of 128 and a group of 16
+    "heads_s": Spec("heads_s", rows=3, ctx=6000, shards=2, interleave=1, k=512,
+                    heads=144, seed=20, row_ends="mixed"),
     # sequence-sharded (PCP) prefill chunk over a replicated fp8 cache: no
     # context sharding; the new K rows are materialised by 3 ranks, gathered
     # and inserted (materialise -> gather -> insert)
