@@ -8,15 +8,15 @@
 //
 // How: a pure streaming kernel — one thread per (row, head, 8 features),
 // fp32 accumulation in partial order, 16-byte bf16 store.  With at most 8
-// partials every load (the partial LSEs and the 16-byte output slices) is
-// issued before the first is used, so a thread makes one memory round trip;
-// more partials are taken four at a time.
+// or 16 partials every load (the partial LSEs and the 16-byte output slices)
+// is issued before the first is used, so a thread makes one memory round
+// trip; more partials are taken four at a time.
 #include "launchers.h"
 
 namespace dsa {
 
 constexpr int kCombineThreads = 256;
-constexpr int kCombineFast = 8;   // partials held in registers at once
+constexpr int kCombineFast = 16;  // most partials held in registers at once
 constexpr float kLog2eC = 1.4426950408889634f;
 
 // acc += w * v for the 8 bf16 values of v; a zero weight (an empty partial,
@@ -34,7 +34,8 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16c(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <bool FAST>
+// NF > 0: up to NF partials, all loads in flight at once; NF == 0: any number
+template <int NF>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
     const uint16_t* __restrict__ pout, const float* __restrict__ plse, int P, int64_t rh_total,
     int dim, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
@@ -49,11 +50,11 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f, M = -INFINITY;
-  if constexpr (FAST) {
-    float l[kCombineFast];
-    uint4 v[kCombineFast];
+  if constexpr (NF > 0) {
+    float l[NF];
+    uint4 v[NF];
 #pragma unroll
-    for (int p = 0; p < kCombineFast; ++p) {
+    for (int p = 0; p < NF; ++p) {
       l[p] = -INFINITY;
       v[p] = make_uint4(0u, 0u, 0u, 0u);
       if (p < P) {
@@ -62,10 +63,10 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
       }
     }
 #pragma unroll
-    for (int p = 0; p < kCombineFast; ++p) M = fmaxf(M, l[p]);
+    for (int p = 0; p < NF; ++p) M = fmaxf(M, l[p]);
     if (M != -INFINITY) {
 #pragma unroll
-      for (int p = 0; p < kCombineFast; ++p) {
+      for (int p = 0; p < NF; ++p) {
         const float w = exp2f((l[p] - M) * kLog2eC);   // exp(-inf) = 0
         z += w;
         accumulate8(acc, w, v[p]);
@@ -112,11 +113,14 @@ int launch_lse_combine(const void* part_out, const float* part_lse, int P, int r
   const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
   const uint16_t* po = reinterpret_cast<const uint16_t*>(part_out);
   uint16_t* o = reinterpret_cast<uint16_t*>(out);
-  if (P <= kCombineFast)
-    hipLaunchKernelGGL(lse_combine_kernel<true>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
+  if (P <= 8)
+    hipLaunchKernelGGL(lse_combine_kernel<8>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
                        stream, po, part_lse, P, rh, dim, o, lse_out);
+  else if (P <= kCombineFast)
+    hipLaunchKernelGGL(lse_combine_kernel<kCombineFast>, dim3((unsigned)blocks),
+                       dim3(kCombineThreads), 0, stream, po, part_lse, P, rh, dim, o, lse_out);
   else
-    hipLaunchKernelGGL(lse_combine_kernel<false>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
+    hipLaunchKernelGGL(lse_combine_kernel<0>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
                        stream, po, part_lse, P, rh, dim, o, lse_out);
   return 0;
 }
