@@ -58,10 +58,8 @@ namespace dsa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnThreads = 512;
@@ -70,9 +68,7 @@ constexpr int kHPW = 16;                       // heads per wave
 constexpr int kHPB = kHPW * kAttnWaves;        // heads per block (128)
 constexpr int kTile = 32;                      // tokens per tile
 constexpr int kRowB = kLatent * 2;             // bf16 row bytes (1152)
-constexpr int kTileB = kTile * kRowB;          // 36864 bytes
 constexpr int kRowB8 = kLatent;                // fp8 row bytes (576)
-constexpr int kTileB8 = kTile * kRowB8;        // 18432 bytes
 constexpr int kQSteps = kLatent / 32;          // 18 k-steps of 32 features
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -123,25 +119,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// ds_read_b64_tr_b8 at LDS byte address addr + OFF.  Written as asm: the
-// compiler guards the builtin form with a full vmcnt wait when it cannot tell
-// the read from the tile gathers still in flight, which would stall every
-// tile on the next two.  The caller waits for the result with lgkm_wait_v.
-template <int OFF>
-__device__ __forceinline__ i32x2_t lds_read_tr8(uint32_t addr) {
-  i32x2_t r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-// ds_read_b64_tr_b16 at LDS byte address addr + OFF, for the same reason
-template <int OFF>
-__device__ __forceinline__ i32x2_t lds_read_tr16(uint32_t addr) {
-  i32x2_t r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-// ds_read_b128 at LDS byte address addr + OFF (as above: the compiler would
-// guard it with a full vmcnt wait behind the tile gathers in flight)
+// LDS reads of the tile operands, written as asm: issued as builtins right
+// after the tile gathers (HBM -> LDS copies counted by vmcnt), the compiler
+// guards them with a full vmcnt wait, because it cannot tell them from the
+// copies still in flight, and the ring would drain every tile.  Each read is
+// at LDS byte address addr + OFF; the caller waits for it with one of the
+// lgkm_wait_* helpers below, which pass the destination registers through
+// the wait so that no use can move above it.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 template <int OFF>
 __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
@@ -149,17 +133,28 @@ __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
-// wait until at most N LDS operations are in flight, passing a and b through
-template <int N>
-__device__ __forceinline__ void lgkm_wait_2(u32x4_t& a, u32x4_t& b) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
-}
-// ds_read_b64 at LDS byte address addr + OFF
 template <int OFF>
 __device__ __forceinline__ i32x2_t lds_read_b64(uint32_t addr) {
   i32x2_t r;
   asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
+}
+template <int OFF>
+__device__ __forceinline__ i32x2_t lds_read_tr16(uint32_t addr) {
+  i32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ i32x2_t lds_read_tr8(uint32_t addr) {
+  i32x2_t r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// wait until at most N LDS operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void lgkm_wait_2(u32x4_t& a, u32x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait_2v(i32x2_t& a, i32x2_t& b) {
@@ -168,12 +163,6 @@ __device__ __forceinline__ void lgkm_wait_2v(i32x2_t& a, i32x2_t& b) {
 template <int N>
 __device__ __forceinline__ void lgkm_wait_4v(i32x2_t& a, i32x2_t& b, i32x2_t& c, i32x2_t& d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
-}
-// wait until at most N LDS operations are in flight; r is passed through the
-// wait so that its uses cannot move above it
-template <int N>
-__device__ __forceinline__ void lgkm_wait_v(i32x2_t& r) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
 }
 
 // 8 e4m3 codes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
