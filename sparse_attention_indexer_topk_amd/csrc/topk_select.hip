@@ -48,18 +48,23 @@ template <int E, bool RESIDENT>
 __device__ __forceinline__ void topk_row(TopkSmem& sm, const float* __restrict__ src, int lo,
                                          int hi, bool vec, int k, int S, int I, int r,
                                          int* __restrict__ oidx, float2* __restrict__ ocand,
-                                         bool out_vec) {
+                                         bool out_vec, const uint32_t* pre) {
   constexpr int NT = kTopkThreads;
   constexpr int kChunk = NT * E;
   const int tid = threadIdx.x;
-  const int base = vec ? (lo & ~3) : lo;
+  // pre: the thread's E logits from local position tid*E on, already loaded
+  // (the whole shard row fits one chunk), so the row starts at position 0
+  const int base = pre ? 0 : (vec ? (lo & ~3) : lo);
   const int nchunks = RESIDENT ? 1 : (hi - base + kChunk - 1) / kChunk;
 
   uint32_t raw[E], key[E];
   uint32_t vmask = 0;   // bit e: element e lies in [lo, hi)
   auto load = [&](int c0) {
     const int p0 = c0 + tid * E;
-    if (vec) {
+    if (pre) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) raw[e] = pre[e];
+    } else if (vec) {
 #pragma unroll
       for (int v = 0; v < E / 4; ++v) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -205,6 +210,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
   const int tid = threadIdx.x;
   const float* src = logits + (int64_t)j * shard_stride + (int64_t)row * ld;
 
+  // A shard row that fits one chunk is requested whole, from local position
+  // 0, before its bounds are known, so that the bounds and the logits arrive
+  // in one memory round trip; [lo, hi) then only masks.  16-byte loads stay
+  // inside the row: ld is a multiple of 4 and at least the local length.
+  constexpr int kChunk = NT * E;
+  const int L = local_count(ctx, r, S, I);
+  const bool whole = vec4 && L <= kChunk;
+  uint32_t pre[E];
+  if (whole) {
+    const int p0 = tid * E;
+#pragma unroll
+    for (int v = 0; v < E / 4; ++v) {
+      // positions past L (masked below) read position 0 instead: no branch
+      const int pp = p0 + 4 * v < L ? p0 + 4 * v : 0;
+      const float4 x = *reinterpret_cast<const float4*>(src + pp);
+      pre[4 * v] = __float_as_uint(x.x);
+      pre[4 * v + 1] = __float_as_uint(x.y);
+      pre[4 * v + 2] = __float_as_uint(x.z);
+      pre[4 * v + 3] = __float_as_uint(x.w);
+    }
+  }
+
   int gs = row_starts ? row_starts[row] : 0;
   int ge = row_ends ? row_ends[row] : ctx;
   gs = gs < 0 ? 0 : (gs > ctx ? ctx : gs);
@@ -230,16 +257,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
     }
     return;
   }
+  if (whole) {
+    topk_row<E, true>(sm, src, lo, hi, true, k, S, I, r, oidx, ocand, cand_vec != 0, pre);
+    return;
+  }
   // 16-byte loads start at the aligned position at or below lo; when that
   // would push a row that fits one chunk past it, the row is loaded
   // element-wise instead
-  constexpr int kChunk = NT * E;
   const bool vec = vec4 && (hi - (lo & ~3) <= kChunk || n > kChunk);
   const int span = hi - (vec ? (lo & ~3) : lo);
   if (span <= kChunk)
-    topk_row<E, true>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0);
+    topk_row<E, true>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0, nullptr);
   else
-    topk_row<E, false>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0);
+    topk_row<E, false>(sm, src, lo, hi, vec, k, S, I, r, oidx, ocand, cand_vec != 0, nullptr);
 }
 
 int launch_topk_select(const float* logits, int64_t ld, int64_t shard_stride, int rows, int ctx,
