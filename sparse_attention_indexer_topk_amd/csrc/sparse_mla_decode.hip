@@ -102,13 +102,6 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
-// Tile layout in LDS (bf16): 36 blocks of 1 KB, block (c / 4) * 2 + t / 16
-// holding tokens 16*(t/16) .. +16 x 16-byte chunks 4*(c/4) .. +4 (32
-// features), token t, chunk c in slot (t % 16) + 16 * (c % 4).  A score k-step
-// then reads one whole block (lane l: token l % 16, chunk l / 16) and a value
-// transpose read 512 contiguous bytes, so neither meets a bank conflict; one
-// gather instruction fills one block.
-
 // compile-time loop: f(IntC<0>{}) .. f(IntC<N-1>{})
 template <int I> struct IntC { static constexpr int value = I; };
 template <int N, int I = 0, class F>
@@ -601,10 +594,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       tile_slots(t + Lay::kAhead, nsv);
       issue(t + Lay::kAhead, nsv);
     }
+    // the two matrix phases run at raised wave priority: where the two waves
+    // of a SIMD are in different phases, the softmax and gather issue of one
+    // yield to the products of the other
+    __builtin_amdgcn_s_setprio(1);
     if (t >= 1) values(t - 1);
     __builtin_amdgcn_sched_barrier(0);
     f32x4_t s0, s1;
     if (t < ntiles) scores(t, s0, s1);
+    __builtin_amdgcn_s_setprio(0);
     if (__builtin_amdgcn_readfirstlane(rflag)) {
       // a reference max moved by more than 2^64: drop the partial sums and
       // replay the token list with the raised reference
