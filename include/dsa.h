@@ -207,8 +207,8 @@ int dsa_merge_convert(const float* cand, int32_t rows, int32_t n_cand, int32_t k
  * out          [n_parts*splits][rows][heads][512] bf16 output.
  * lse          [n_parts*splits][rows][heads] fp32 output.
  * Errors: INVALID_ARG (null pointers, heads not a positive multiple of 16,
- * splits outside [1, 64], sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache
- * not bf16/fp8).
+ * splits outside [1, 64], rows*n_parts*splits*ceil(heads/128) above
+ * 2^31 - 1, sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache not bf16/fp8).
  */
 int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads,
                           const void* cache, int32_t cache_dtype,

@@ -167,6 +167,11 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void
   if (cache_dtype == DSA_FP8_E4M3 && !cache_scale)
     return fail(DSA_ERR_INVALID_ARG, "%s: fp8 cache needs cache_scale", fn);
   if (num_slots < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_slots < 0", fn);
+  // the kernel numbers its workgroups (rows x parts x splits x head groups of
+  // 128) with 32-bit integers
+  if ((int64_t)rows * n_parts * splits * ((heads + 127) / 128) > 0x7fffffffLL)
+    return fail(DSA_ERR_INVALID_ARG, "%s: rows x n_parts x splits x head groups exceeds 2^31 - 1",
+                fn);
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(slots, 4) ||
       !aligned(lse, 4) || !aligned(cache_scale, 4))
     return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer (q, cache, out need 16 bytes)", fn);

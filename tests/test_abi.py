@@ -121,6 +121,9 @@ def test_sparse_mla_decode_rejects():
     assert call(splits=65) == INV
     assert call(splits=8) == OK
     assert call(rows=-3) == INV
+    # workgroup count past 2^31 - 1 is refused before any launch
+    assert call(rows=1 << 29, parts=4, heads=128) == INV
+    assert call(rows=1 << 28, parts=4, splits=2, heads=128) == INV
 
 
 def test_lse_combine_rejects():
