@@ -213,10 +213,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
   // A shard row that fits one chunk is requested whole, from local position
   // 0, before its bounds are known, so that the bounds and the logits arrive
   // in one memory round trip; [lo, hi) then only masks.  16-byte loads stay
-  // inside the row: ld is a multiple of 4 and at least the local length.
+  // inside the row: ld is a multiple of 4 and at least the local length.  An
+  // empty shard row reads nothing (ld may then be 0).
   constexpr int kChunk = NT * E;
   const int L = local_count(ctx, r, S, I);
-  const bool whole = vec4 && L <= kChunk;
+  const bool whole = vec4 && L > 0 && L <= kChunk;
   uint32_t pre[E];
   if (whole) {
     const int p0 = tid * E;

@@ -139,6 +139,17 @@ def test_topk_small_and_boundary_rows():
     check_topk(g, starts, ends, k, S, I)
 
 
+def test_topk_empty_shards():
+    # a context shorter than one interleave period: shards 2 and 3 own no
+    # position, shard 1 a partial block
+    S, I, C, k = 4, 64, 100, 512
+    g = normal(3, C, 6)
+    starts = np.array([0, 0, 70], np.int32)
+    ends = np.array([C, 50, C], np.int32)
+    log("topk empty shards")
+    check_topk(g, starts, ends, k, S, I)
+
+
 def test_topk_element_loads_and_chunked_rows():
     # one shard of 20000 positions: the 16K-per-thread kernel streams it in
     # chunks; a row starting at 3 with 16384 valid positions fits one chunk
