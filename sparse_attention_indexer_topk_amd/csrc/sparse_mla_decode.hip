@@ -277,9 +277,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   // ---- startup: count and the first tiles' slot entries ------------------------
   const int* my_slots = slots + ((int64_t)part * rows + row) * k;
   int cnt = counts ? counts[(int64_t)part * rows + row] : k;
-  bf16x8_t qf[kQSteps];   // loaded after the first gathers are issued
+  bf16x8_t qf[kQSteps];
   int sl0 = 0;
   if (splits == 1 && tid < kSlotInit * kTile) sl0 = my_slots[tid];   // k >= 512
+  // q is requested next: it arrives while the slot entries are published and
+  // the first gathers go out
+  const uint16_t* qp = q + ((int64_t)row * heads + (wave_on ? head : 0)) * kLatent + 8 * g4;
+#pragma unroll
+  for (int kk = 0; kk < kQSteps; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
   cnt = cnt < 0 ? 0 : (cnt > k ? k : cnt);
   if (num_slots <= 0) cnt = 0;
   // this split's slice of the part's token list
@@ -298,7 +304,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       s_sring[tid] = s;
     }
   };
-  load_first_slots(splits == 1);
+  // the first slot entries go to LDS in two separate branches, so that the
+  // common one waits for its own load only and q stays in flight
+  if (splits == 1) {
+    if (tid < kSlotInit * kTile) s_sring[tid] = sl0;
+  } else {
+    load_first_slots(false);
+  }
 
   f32x4_t o[kFBW][kNHB];
 #pragma unroll
@@ -558,12 +570,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
       if (u < ntiles) issue(u, sv[u]);
   };
   start();
-  // q is requested after the first tiles' gathers, and everything in flight
-  // is waited for before the loop, so that inside it q is plain registers
-  const uint16_t* qp = q + ((int64_t)row * heads + (wave_on ? head : 0)) * kLatent + 8 * g4;
-#pragma unroll
-  for (int kk = 0; kk < kQSteps; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(qp + 32 * kk));
+  // everything in flight (q, the first tiles) is waited for before the loop,
+  // so that inside it q is plain registers
   asm volatile("s_waitcnt vmcnt(0)"
                : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
                  "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]),
