@@ -107,9 +107,11 @@ def convert_index(ids, row_req, block_table, block_size, S, I, first=0, count=No
     ``row_req``: request of each row (None = identity).
     Returns ``slots [count][R][k]`` int32, ``counts [count][R]`` int32.
 
-    Guards the pages leave open (the page's kernel is handed a table that
-    covers every id): a row whose request is outside ``[0, Rq)`` keeps
-    nothing, and an id whose block column is ``>= W`` is dropped.
+    Outside the pages' domain (a reading, not a statement of the pages: the
+    page's kernel is handed a table that covers every id it sees): a row
+    whose request is outside ``[0, Rq)`` keeps nothing, and an id whose block
+    column is ``>= W`` is dropped.  Inside the domain neither rule changes a
+    result.
     """
     count = S - first if count is None else count
     R, k = ids.shape

@@ -142,3 +142,45 @@ def test_insert_layout_and_skip(cache_dtype):
     for s in range(flat.shape[0]):
         if s not in touched:
             assert np.all(flat[s] == 0)
+
+
+# ------------------------------------------------------- RoPE table ----
+# The table is an input that both sides receive, so parity alone cannot see a
+# wrong frequency in it.  It is pinned from the definition instead: with base
+# 10000 over 64 rotary dimensions pair i turns by 10000^(-2i/64) = 10^(-i/8)
+# radians per position, so pairs 8, 16 and 24 turn by exactly 0.1, 0.01 and
+# 0.001, and positions 10, 100 and 1000 put each of them at an angle of one
+# radian; pair 0 turns by one radian per position for any base.
+def _check_rope_table(cs):
+    c1, s1 = np.float32(np.cos(1.0)), np.float32(np.sin(1.0))
+    assert cs.shape[1] == 64 and cs.dtype == np.float32
+    for pos, pair in ((1, 0), (10, 8), (100, 16), (1000, 24)):
+        assert cs[pos, pair] == c1, f"cos of pair {pair} at position {pos}"
+        assert cs[pos, 32 + pair] == s1, f"sin of pair {pair} at position {pos}"
+    # position 0 is the identity rotation for every pair
+    assert np.all(cs[0, :32] == 1.0) and np.all(cs[0, 32:] == 0.0)
+
+
+def test_rope_table_frequencies_from_the_definition():
+    _check_rope_table(dsa_inputs._cos_sin_table(1001))
+
+
+def test_rope_table_of_the_fp8_workload():
+    c = dsa_inputs.make(dsa_inputs.spec("fp8_s"), with_cache=False)
+    _check_rope_table(c.cos_sin)
+    assert c.cos_sin.shape[0] == c.ctx          # one row per context position
+
+
+def _planted_table(n_pos, inv_freq):
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@pytest.mark.parametrize("what,inv_freq", [
+    ("base 1000", 1000.0 ** (-2.0 * np.arange(32) / 64)),
+    ("exponent -i/64", 10000.0 ** (-1.0 * np.arange(32) / 64)),
+    ("pairs shifted by one", 10000.0 ** (-2.0 * (np.arange(32) + 1) / 64)),
+])
+def test_planted_rope_table_mistakes_are_caught(what, inv_freq):
+    with pytest.raises(AssertionError):
+        _check_rope_table(_planted_table(1001, inv_freq))
