@@ -123,6 +123,15 @@ PARITY_CASES = {
     "pcp_s": Spec("pcp_s", rows=24, ctx=3000, shards=1, interleave=1, k=512,
                   heads=16, seed=19, logits="causal", one_request=True,
                   row_ends="causal", q_pos_step=113, cache="fp8", prologue=True, pcp=3),
+    # sequence-sharded prologue over 3 ranks combined with a context sharded
+    # over 2 shards (PCP x DCP): materialise -> gather -> insert, then the
+    # per-shard top-K, merge, attention and the combine of the shard partials
+    "pcp_dcp_s": Spec("pcp_dcp_s", rows=6, ctx=4100, shards=2, interleave=1, k=512,
+                      heads=32, seed=22, cache="fp8", prologue=True, pcp=3,
+                      row_ends="mixed"),
+    # the most shards the library takes: 16 shards of interleave 2
+    "s16_s": Spec("s16_s", rows=3, ctx=12007, shards=16, interleave=2, k=512,
+                  heads=16, seed=21, row_ends="mixed"),
 }
 
 

@@ -111,11 +111,103 @@ def _bits16(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _shape(t: torch.Tensor, name: str, shape):
+    """``shape``: expected sizes, None = any."""
+    if t.dim() != len(shape) or any(e is not None and a != e for a, e in zip(t.shape, shape)):
+        want = "[" + "][".join("*" if e is None else str(e) for e in shape) + "]"
+        raise RuntimeError(f"{name} must be {want} (got {list(t.shape)})")
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+
+
+def _row_major(t: torch.Tensor, name: str):
+    """Rows may be strided (a leading dimension), elements of a row may not;
+    the leading strides must not make rows overlap."""
+    if t.dim() > 0 and t.stride(-1) != 1:
+        raise RuntimeError(f"{name} must have a unit innermost stride")
+    for d in range(t.dim() - 1):
+        inner = t.stride(d + 1) * t.shape[d + 1] if d + 1 < t.dim() else 1
+        if t.shape[d] > 1 and t.stride(d) < inner:
+            raise RuntimeError(f"{name}: dimension {d} overlaps the next (stride {t.stride(d)})")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise RuntimeError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
 def version() -> int:
     return lib().dsa_version()
 
 
 # ---------------------------------------------------------------------------
+# Every wrapper checks dtype, device, shape, length and contiguity against
+# what the kernels index before it calls the library, so a mis-sized tensor
+# raises here instead of becoming an out-of-bounds device access.
+
+def _check_block_table(block_table: torch.Tensor):
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 3:
+        raise RuntimeError("block_table must be [shard_count][num_reqs][width]")
+    # the kernels take the row stride as the table width
+    if block_table.stride(1) != block_table.shape[2]:
+        raise RuntimeError("block_table rows must be dense (row stride == width)")
+    _row_major(block_table, "block_table")
+
+
+def _bt_shard_stride(block_table: torch.Tensor) -> int:
+    count, num_reqs, width = block_table.shape
+    return block_table.stride(0) if count > 1 else num_reqs * width
+
+
+def _check_slot_outputs(slots, counts, count, rows, k):
+    _need(slots, "slots", torch.int32)
+    _shape(slots, "slots", (count, rows, k))
+    _contig(slots, "slots")
+    if counts is not None:
+        _need(counts, "counts", torch.int32)
+        _shape(counts, "counts", (count, rows))
+        _contig(counts, "counts")
+
+
+def _check_cand(cand: torch.Tensor, name="cand"):
+    _need(cand, name, torch.float32)
+    if cand.dim() != 3 or cand.shape[2] != 2:
+        raise RuntimeError(f"{name} must be [rows][n_cand][2] (got {list(cand.shape)})")
+    _contig(cand, name)
+
+
+def _check_row_vec(t, name, rows, dtype=torch.int32):
+    if t is not None:
+        _need(t, name, dtype)
+        _shape(t, name, (rows,))
+        _contig(t, name)
+
+
+def _check_cache(cache: torch.Tensor):
+    _need(cache, "cache")
+    if cache.dim() < 1 or cache.shape[-1] != 576:
+        raise RuntimeError(f"cache entries must be 576 wide (got {list(cache.shape)})")
+    _contig(cache, "cache")
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    _bits16(cache, "cache")
+    return DSA_BF16
+
+
+def _check_scale(cache_scale, cdt):
+    if cdt == DSA_FP8_E4M3:
+        if cache_scale is None:
+            raise RuntimeError("an fp8 cache needs cache_scale")
+        _need(cache_scale, "cache_scale", torch.float32)
+        if cache_scale.numel() < 1:
+            raise RuntimeError("cache_scale must hold one value")
+
+
 def topk_select(logits: torch.Tensor, k: int, *, ctx: int, num_shards: int, interleave: int,
                 row_starts: Optional[torch.Tensor] = None, row_ends: Optional[torch.Tensor] = None,
                 shard_first: int = 0, local_idx: Optional[torch.Tensor] = None,
@@ -125,10 +217,14 @@ def topk_select(logits: torch.Tensor, k: int, *, ctx: int, num_shards: int, inte
     _need(logits, "logits", torch.float32)
     if logits.dim() != 3:
         raise RuntimeError("logits must be [shard_count][rows][ld]")
+    _row_major(logits, "logits")
+    # the kernel takes the row stride as the row length (and may read up to
+    # it with 16-byte loads), so rows must be dense
+    if logits.stride(1) != logits.shape[2]:
+        raise RuntimeError("logits rows must be dense (row stride == ld)")
     count, rows, _ = logits.shape
-    for name, t in (("row_starts", row_starts), ("row_ends", row_ends)):
-        if t is not None:
-            _need(t, name, torch.int32)
+    _check_row_vec(row_starts, "row_starts", rows)
+    _check_row_vec(row_ends, "row_ends", rows)
     dev = logits.device
     if local_idx is None and want_local_idx:
         local_idx = torch.empty((count, rows, k), dtype=torch.int32, device=dev)
@@ -136,8 +232,12 @@ def topk_select(logits: torch.Tensor, k: int, *, ctx: int, num_shards: int, inte
         cand = torch.empty((rows, num_shards * k, 2), dtype=torch.float32, device=dev)
     if local_idx is not None:
         _need(local_idx, "local_idx", torch.int32)
+        _shape(local_idx, "local_idx", (count, rows, k))
+        _contig(local_idx, "local_idx")
     if cand is not None:
-        _need(cand, "cand", torch.float32)
+        _check_cand(cand)
+        _shape(cand, "cand", (rows, num_shards * k, 2))
+    _same_device(logits, row_starts, row_ends, local_idx, cand)
     _check(lib().dsa_topk_select(
         _ptr(logits), logits.stride(1), logits.stride(0) if count > 1 else rows * logits.stride(1),
         rows, ctx, _ptr(row_starts), _ptr(row_ends), k, num_shards, interleave, shard_first, count,
@@ -148,13 +248,14 @@ def topk_select(logits: torch.Tensor, k: int, *, ctx: int, num_shards: int, inte
 def merge_candidates(cand: torch.Tensor, k: int, *, id_bound: int,
                      ids: Optional[torch.Tensor] = None, stream=None):
     """Global stable top-K over ``cand`` [rows][n_cand][2] fp32 -> ids [rows][k]."""
-    _need(cand, "cand", torch.float32)
-    if not cand.is_contiguous():
-        raise RuntimeError("cand must be contiguous")
+    _check_cand(cand)
     rows, n_cand, _ = cand.shape
     if ids is None:
         ids = torch.empty((rows, k), dtype=torch.int32, device=cand.device)
     _need(ids, "ids", torch.int32)
+    _shape(ids, "ids", (rows, k))
+    _contig(ids, "ids")
+    _same_device(cand, ids)
     _check(lib().dsa_merge_candidates(_ptr(cand), rows, n_cand, k, id_bound, _ptr(ids),
                                       _stream(stream)))
     return ids
@@ -170,28 +271,26 @@ def merge_convert(cand: torch.Tensor, k: int, block_table: torch.Tensor, *, id_b
     cand [rows][n_cand][2] fp32 -> (ids [rows][k] or None, slots
     [shard_count][rows][k], counts [shard_count][rows]).
     """
-    _need(cand, "cand", torch.float32)
-    _need(block_table, "block_table", torch.int32)
-    if not cand.is_contiguous():
-        raise RuntimeError("cand must be contiguous")
+    _check_cand(cand)
+    _check_block_table(block_table)
     rows, n_cand, _ = cand.shape
     count, num_reqs, _ = block_table.shape
-    if row_req is not None:
-        _need(row_req, "row_req", torch.int32)
+    _check_row_vec(row_req, "row_req", rows)
     if ids is None and want_ids:
         ids = torch.empty((rows, k), dtype=torch.int32, device=cand.device)
     if ids is not None:
         _need(ids, "ids", torch.int32)
+        _shape(ids, "ids", (rows, k))
+        _contig(ids, "ids")
     if slots is None:
         slots = torch.empty((count, rows, k), dtype=torch.int32, device=cand.device)
     if counts is None:
         counts = torch.empty((count, rows), dtype=torch.int32, device=cand.device)
-    _need(slots, "slots", torch.int32)
-    _need(counts, "counts", torch.int32)
+    _check_slot_outputs(slots, counts, count, rows, k)
+    _same_device(cand, block_table, row_req, ids, slots, counts)
     _check(lib().dsa_merge_convert(
         _ptr(cand), rows, n_cand, k, id_bound, _ptr(ids), _ptr(row_req), num_reqs,
-        _ptr(block_table), block_table.stride(1),
-        block_table.stride(0) if count > 1 else num_reqs * block_table.stride(1), block_size,
+        _ptr(block_table), block_table.stride(1), _bt_shard_stride(block_table), block_size,
         num_shards, interleave, shard_first, count, _ptr(slots), _ptr(counts), _stream(stream)))
     return ids, slots, counts
 
@@ -202,23 +301,23 @@ def convert_index(ids: torch.Tensor, block_table: torch.Tensor, *, block_size: i
                   counts: Optional[torch.Tensor] = None, stream=None):
     """ids [rows][k] -> slots [shard_count][rows][k], counts [shard_count][rows]."""
     _need(ids, "ids", torch.int32)
-    _need(block_table, "block_table", torch.int32)
-    if not ids.is_contiguous():
-        raise RuntimeError("ids must be contiguous")
+    if ids.dim() != 2:
+        raise RuntimeError("ids must be [rows][k]")
+    _contig(ids, "ids")
+    _check_block_table(block_table)
     rows, k = ids.shape
     count, num_reqs, _ = block_table.shape
-    if row_req is not None:
-        _need(row_req, "row_req", torch.int32)
+    _check_row_vec(row_req, "row_req", rows)
     if slots is None:
         slots = torch.empty((count, rows, k), dtype=torch.int32, device=ids.device)
     if counts is None:
         counts = torch.empty((count, rows), dtype=torch.int32, device=ids.device)
-    _need(slots, "slots", torch.int32)
-    _need(counts, "counts", torch.int32)
+    _check_slot_outputs(slots, counts, count, rows, k)
+    _same_device(ids, block_table, row_req, slots, counts)
     _check(lib().dsa_convert_index(
         _ptr(ids), rows, k, _ptr(row_req), num_reqs, _ptr(block_table), block_table.stride(1),
-        block_table.stride(0) if count > 1 else num_reqs * block_table.stride(1), block_size,
-        num_shards, interleave, shard_first, count, _ptr(slots), _ptr(counts), _stream(stream)))
+        _bt_shard_stride(block_table), block_size, num_shards, interleave, shard_first, count,
+        _ptr(slots), _ptr(counts), _stream(stream)))
     return slots, counts
 
 
@@ -232,30 +331,36 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
     bf16 and lse [n_parts*splits][rows][heads] fp32 (split-K partials of part p
     are p*splits .. p*splits + splits - 1)."""
     _bits16(q, "q")
-    _need(cache, "cache")
+    if q.dim() != 3 or q.shape[2] != 576:
+        raise RuntimeError(f"q must be [rows][heads][576] (got {list(q.shape)})")
+    _contig(q, "q")
+    cdt = _check_cache(cache)
+    _check_scale(cache_scale, cdt)
     _need(slots, "slots", torch.int32)
-    if not (q.is_contiguous() and cache.is_contiguous() and slots.is_contiguous()):
-        raise RuntimeError("q, cache and slots must be contiguous")
+    if slots.dim() != 3:
+        raise RuntimeError("slots must be [n_parts][rows][k]")
+    _contig(slots, "slots")
     rows, heads, _ = q.shape
-    n_parts, _, k = slots.shape
-    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
-        cdt = DSA_FP8_E4M3
-        if cache_scale is None:
-            raise RuntimeError("an fp8 cache needs cache_scale")
-        _need(cache_scale, "cache_scale", torch.float32)
-    else:
-        _bits16(cache, "cache")
-        cdt = DSA_BF16
+    n_parts, s_rows, k = slots.shape
+    if s_rows != rows:
+        raise RuntimeError(f"slots has {s_rows} rows, q has {rows}")
     num_slots = cache.numel() // 576
     if counts is not None:
         _need(counts, "counts", torch.int32)
+        _shape(counts, "counts", (n_parts, rows))
+        _contig(counts, "counts")
+    P = n_parts * int(splits)
     if out is None:
-        out = torch.empty((n_parts * splits, rows, heads, 512), dtype=torch.bfloat16,
-                          device=q.device)
+        out = torch.empty((P, rows, heads, 512), dtype=torch.bfloat16, device=q.device)
     if lse is None:
-        lse = torch.empty((n_parts * splits, rows, heads), dtype=torch.float32, device=q.device)
+        lse = torch.empty((P, rows, heads), dtype=torch.float32, device=q.device)
     _bits16(out, "out")
+    _shape(out, "out", (P, rows, heads, 512))
+    _contig(out, "out")
     _need(lse, "lse", torch.float32)
+    _shape(lse, "lse", (P, rows, heads))
+    _contig(lse, "lse")
+    _same_device(q, cache, slots, counts, cache_scale, out, lse)
     _check(lib().dsa_sparse_mla_decode(
         _ptr(q), rows, heads, _ptr(cache), cdt, _ptr(cache_scale), num_slots, _ptr(slots),
         _ptr(counts), k, n_parts, int(splits), float(sm_scale), _ptr(out), _ptr(lse),
@@ -269,16 +374,41 @@ def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, *,
     """part_out [n_parts][rows][heads][dim] bf16, part_lse [n_parts][rows][heads]."""
     _bits16(part_out, "part_out")
     _need(part_lse, "part_lse", torch.float32)
-    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
-        raise RuntimeError("partials must be contiguous")
+    if part_out.dim() != 4:
+        raise RuntimeError("part_out must be [n_parts][rows][heads][dim]")
+    _contig(part_out, "part_out")
     n_parts, rows, heads, dim = part_out.shape
+    _shape(part_lse, "part_lse", (n_parts, rows, heads))
+    _contig(part_lse, "part_lse")
     if out is None:
         out = torch.empty((rows, heads, dim), dtype=torch.bfloat16, device=part_out.device)
     if lse_out is None and want_lse:
         lse_out = torch.empty((rows, heads), dtype=torch.float32, device=part_out.device)
+    _bits16(out, "out")
+    _shape(out, "out", (rows, heads, dim))
+    _contig(out, "out")
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32)
+        _shape(lse_out, "lse_out", (rows, heads))
+        _contig(lse_out, "lse_out")
+    _same_device(part_out, part_lse, out, lse_out)
     _check(lib().dsa_lse_combine(_ptr(part_out), _ptr(part_lse), n_parts, rows, heads, dim,
                                  _ptr(out), _ptr(lse_out), _stream(stream)))
     return out, lse_out
+
+
+def _check_rows_in(kv_c, k_pe):
+    _bits16(kv_c, "kv_c")
+    _bits16(k_pe, "k_pe")
+    if kv_c.dim() != 2 or kv_c.shape[1] < 512:
+        raise RuntimeError(f"kv_c must be [T][>=512] (got {list(kv_c.shape)})")
+    if k_pe.dim() != 2 or k_pe.shape[1] < 64:
+        raise RuntimeError(f"k_pe must be [T][>=64] (got {list(k_pe.shape)})")
+    if k_pe.shape[0] != kv_c.shape[0]:
+        raise RuntimeError(f"kv_c has {kv_c.shape[0]} rows, k_pe has {k_pe.shape[0]}")
+    _row_major(kv_c, "kv_c")
+    _row_major(k_pe, "k_pe")
+    return kv_c.shape[0]
 
 
 def fused_rmsnorm_rope(kv_c: torch.Tensor, k_pe: torch.Tensor, rms_w: torch.Tensor, eps: float,
@@ -290,19 +420,29 @@ def fused_rmsnorm_rope(kv_c: torch.Tensor, k_pe: torch.Tensor, rms_w: torch.Tens
                        slot_mapping: Optional[torch.Tensor] = None, stream=None):
     """RMSNorm(kv_c) + RoPE(k_pe); writes the given outputs and/or inserts into
     ``cache`` at ``slot_mapping``.  Returns (kv_c_out, k_pe_out)."""
-    _bits16(kv_c, "kv_c")
-    _bits16(k_pe, "k_pe")
+    T = _check_rows_in(kv_c, k_pe)
     _bits16(rms_w, "rms_w")
+    _shape(rms_w, "rms_w", (512,))
+    _contig(rms_w, "rms_w")
     _need(cos_sin, "cos_sin", torch.float32)
-    _need(positions, "positions", torch.int32)
-    T = kv_c.shape[0]
+    _shape(cos_sin, "cos_sin", (None, 64))
+    _contig(cos_sin, "cos_sin")
+    _check_row_vec(positions, "positions", T)
+    for name, t, w in (("kv_c_out", kv_c_out, 512), ("k_pe_out", k_pe_out, 64)):
+        if t is not None:
+            _bits16(t, name)
+            _shape(t, name, (T, w))
+            _contig(t, name)
     cdt, num_slots = 0, 0
     if slot_mapping is not None:
-        _need(slot_mapping, "slot_mapping", torch.int64)
+        _check_row_vec(slot_mapping, "slot_mapping", T, torch.int64)
         if cache is None:
             raise RuntimeError("slot_mapping needs a cache")
-        cdt = DSA_FP8_E4M3 if cache.dtype in (torch.uint8, torch.float8_e4m3fn) else DSA_BF16
+        cdt = _check_cache(cache)
+        _check_scale(cache_scale, cdt)
         num_slots = cache.numel() // 576
+    _same_device(kv_c, k_pe, rms_w, cos_sin, positions, kv_c_out, k_pe_out, cache, cache_scale,
+                 slot_mapping)
     _check(lib().dsa_fused_rmsnorm_rope(
         _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), T, _ptr(rms_w), float(eps),
         _ptr(cos_sin), cos_sin.shape[0], _ptr(positions), _ptr(kv_c_out), _ptr(k_pe_out),
@@ -315,11 +455,11 @@ def cache_insert(kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
                  stream=None):
     """Write materialised K rows (kv_c [T][512], k_pe [T][64] bf16) into ``cache``
     at ``slot_mapping`` (bf16, or fp8 e4m3 scaled by ``cache_scale``)."""
-    _bits16(kv_c, "kv_c")
-    _bits16(k_pe, "k_pe")
-    _need(slot_mapping, "slot_mapping", torch.int64)
-    T = kv_c.shape[0]
-    cdt = DSA_FP8_E4M3 if cache.dtype in (torch.uint8, torch.float8_e4m3fn) else DSA_BF16
+    T = _check_rows_in(kv_c, k_pe)
+    _check_row_vec(slot_mapping, "slot_mapping", T, torch.int64)
+    cdt = _check_cache(cache)
+    _check_scale(cache_scale, cdt)
+    _same_device(kv_c, k_pe, cache, slot_mapping, cache_scale)
     _check(lib().dsa_cache_insert(
         _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), T, _ptr(cache), cdt,
         _ptr(cache_scale), _ptr(slot_mapping), cache.numel() // 576, _stream(stream)))

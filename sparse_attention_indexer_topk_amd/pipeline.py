@@ -63,6 +63,8 @@ class DecodePath:
         if splits is None:   # enough workgroups to cover the 256 CUs
             blocks = R * S * ((H + 127) // 128)
             splits = max(1, min(8, -(-256 // blocks)))
+        # the combine merges at most 64 partials per (row, head)
+        splits = max(1, min(splits, 64 // S))
         self.splits = splits
         self.cand = torch.empty((R, S * k, 2), dtype=torch.float32, device=dev)
         self.local_idx = torch.empty((S, R, k), dtype=torch.int32, device=dev)

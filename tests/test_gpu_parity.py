@@ -3,7 +3,8 @@
 * every small parity case, element by element at every stage (prologue,
   top-K + candidates, merge, convert, partial attention, combine);
 * the five full-size workloads in the launch configuration the benchmark
-  times, on sampled rows the oracle computes one by one;
+  times: every row of the decode, long and fp8 workloads at every stage, and
+  256 (integer stages) and 18 (attention) rows spread over the prefill chunk;
 * determinism: two runs are bit-identical.
 """
 import sys
@@ -149,20 +150,34 @@ def check_attention(c, path, splits, opo, opl, oo, ol, ocounts):
     assert not bad, f"combined (splits={splits}): {bad}"
 
 
-def sample_rows(name, R):
-    if name == "prefill":
-        picks = [0, 1, 2, 3, 63, 511, 2046, 2047, 2048, 2049, 4095, 6000, 8190, 8191]
-    else:
-        picks = [0, 1, R // 2, R - 1]
+def integer_rows(name, R):
+    """Rows whose selection, merge and conversion are compared bit for bit:
+    every row, except on prefill (8192 rows), where 256 rows spread over the
+    chunk plus the short-row boundary are."""
+    if name != "prefill":
+        return np.arange(R, dtype=np.int64)
+    picks = {0, 1, 2, 3, 63, 511, 2046, 2047, 2048, 2049, 4095, 8190, 8191}
+    picks |= set(np.linspace(0, R - 1, 256).round().astype(int).tolist())
+    picks |= set(attention_rows(name, R).tolist())
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def attention_rows(name, R):
+    """Rows whose partial and combined attention is compared: every row,
+    except on prefill, where the oracle's fp64 attention over 8192 rows would
+    take too long and 18 rows spread over the chunk are compared."""
+    if name != "prefill":
+        return np.arange(R, dtype=np.int64)
+    picks = [0, 1, 2, 3, 63, 511, 2046, 2047, 2048, 2049, 4095, 6000, 8190, 8191]
     rng = np.random.default_rng(123)
-    picks += rng.choice(R, min(R, 4), replace=False).tolist()
-    return np.array(sorted({p for p in picks if p < R}), dtype=np.int64)
+    picks += rng.choice(R, 4, replace=False).tolist()
+    return np.array(sorted(set(picks)), dtype=np.int64)
 
 
 @pytest.mark.slow
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(dsa_inputs.CONFIGS))
-def test_full_size_workload_sampled_rows(name):
+def test_full_size_workload(name):
     log(f"[full] workload {name}: generating")
     c = dsa_inputs.make(name)
     path = DecodePath(**dsa_inputs.device_arrays(c))
@@ -175,11 +190,12 @@ def test_full_size_workload_sampled_rows(name):
     path.run_attention()
     path.run_combine()
     torch.cuda.synchronize()
-    rs = sample_rows(name, c.rows)
-    log(f"[full] workload {name}: oracle on rows {rs.tolist()}")
     if rows_oracle is not None:
         flat = c.cache.reshape(-1, 576)
         flat[c.slot_mapping] = rows_oracle        # in place: the host copy is ours
+
+    rs = integer_rows(name, c.rows)
+    log(f"[full] workload {name}: selection, merge, conversion on {len(rs)} rows")
     _, ocand = oracle.topk_select(c.logits[:, rs], c.row_starts[rs], c.row_ends[rs], c.ctx, c.k,
                                   c.S, c.I)
     gcand = path.cand[torch.from_numpy(rs).cuda()].cpu().numpy()
@@ -189,16 +205,21 @@ def test_full_size_workload_sampled_rows(name):
     oslots, ocounts = oracle.convert_index(oids, c.row_req[rs], c.block_table, 64, c.S, c.I)
     assert np.array_equal(path.slots.cpu().numpy()[:, rs], oslots)
     assert np.array_equal(path.counts.cpu().numpy()[:, rs], ocounts)
-    opo, opl = oracle.sparse_mla_partial(c.q[rs], c.cache, c.cache_dtype, c.cache_scale, oslots,
-                                         ocounts, c.sm_scale)
-    gpo = bf16_bits_to_f64(bits16(path.pout[:, torch.from_numpy(rs).cuda()]))
-    gpl = path.plse.cpu().numpy()[:, rs].astype(np.float64)
+
+    ar = attention_rows(name, c.rows)
+    pos = np.searchsorted(rs, ar)
+    assert np.array_equal(rs[pos], ar)
+    log(f"[full] workload {name}: attention and combine on {len(ar)} rows")
+    opo, opl = oracle.sparse_mla_partial(c.q[ar], c.cache, c.cache_dtype, c.cache_scale,
+                                         oslots[:, pos], ocounts[:, pos], c.sm_scale)
+    gpo = bf16_bits_to_f64(bits16(path.pout[:, torch.from_numpy(ar).cuda()]))
+    gpl = path.plse.cpu().numpy()[:, ar].astype(np.float64)
     gpo, gpl = split_partials_to_parts(gpo, gpl, c.S, path.splits)
     bad = attn_mismatch(gpo, opo, gpl, opl)
     assert not bad, f"partials: {bad}"
     oo, ol = oracle.lse_combine(opo, opl)
-    go = bf16_bits_to_f64(bits16(path.out[torch.from_numpy(rs).cuda()]))
-    bad = attn_mismatch(go, oo, path.lse.cpu().numpy()[rs], ol)
+    go = bf16_bits_to_f64(bits16(path.out[torch.from_numpy(ar).cuda()]))
+    bad = attn_mismatch(go, oo, path.lse.cpu().numpy()[ar], ol)
     assert not bad, f"combined: {bad}"
     log(f"[full] workload {name}: ok")
 
