@@ -24,7 +24,8 @@ Module map:
 * ``select``    — per-shard stable top-K with candidate packing, global
                   merge, global-to-local index conversion with compaction;
 * ``attention`` — sparse MLA partial attention with base-e LSE, LSE combine;
-* ``prologue``  — RMSNorm + interleaved-pair RoPE, cache insert;
+* ``prologue``  — RMSNorm + interleaved-pair RoPE, cache insert; the same
+                  for the indexer key (materialise, fp8 indexer-cache insert);
 * ``formats``   — bf16 and fp8 e4m3 encode/decode written from their
                   definitions.
 
@@ -35,12 +36,12 @@ that no such check can pin are marked "parity unpinned" where they occur.
 from .maps import owner, local, global_id, local_count
 from .select import topk_select, merge_candidates, convert_index, unsharded_topk
 from .attention import sparse_mla_partial, lse_combine, attention_over_ids
-from .prologue import rmsnorm_rope, cache_insert
+from .prologue import rmsnorm_rope, cache_insert, index_norm_rope, index_cache_insert
 from . import formats
 
 __all__ = [
     "owner", "local", "global_id", "local_count",
     "topk_select", "merge_candidates", "convert_index", "unsharded_topk",
     "sparse_mla_partial", "lse_combine", "attention_over_ids",
-    "rmsnorm_rope", "cache_insert", "formats",
+    "rmsnorm_rope", "cache_insert", "index_norm_rope", "index_cache_insert", "formats",
 ]

@@ -29,6 +29,7 @@ from .formats import bf16_to_f64, f64_to_bf16, f64_to_e4m3
 
 D_V = 512
 D_ROPE = 64
+D_INDEX = 128
 
 
 def rmsnorm_rope(kv_c, k_pe, w, eps, cos_sin, positions):
@@ -61,4 +62,50 @@ def cache_insert(cache, slot_mapping, kv_c_out, k_pe_out, cache_dtype, scale):
             flat[slot] = f64_to_e4m3(bf16_to_f64(entry) / np.float64(scale))
         else:
             flat[slot] = entry
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Indexer-key branch (pid == 0 of the same fused kernel).
+#
+# PR #52046 report, 实现拆解 item 1: the indexer-K branch materialises the
+# indexer key into ``index_k_out`` when that output is given, and quantises it
+# to FP8 and writes it into the indexer cache only when both the indexer cache
+# and the slot mapping are given.  The pages do not print this branch's
+# arithmetic; readings taken (the plainest ones the page's other branch
+# supports):
+# * the key is 128 wide: 64 unrotated dimensions followed by a 64-dimension
+#   rotary part (the order of the latent entry, kv_c before k_pe);
+# * "norm" is the kernel's only norm, RMSNorm, over all 128 dimensions with
+#   the branch's own multiplicative weight and epsilon; RoPE rotates the
+#   normalised rotary part in interleaved pairs with the same cos/sin table
+#   and position as the latent branch; evaluated exactly, rounded once to
+#   bf16;
+# * FP8 quantisation is the page's quant of the latent branch, e4m3(value /
+#   scale) with a per-tensor scale, applied to the materialised bf16 values.
+
+def index_norm_rope(index_k, w, eps, cos_sin, positions):
+    """Returns the materialised indexer keys as bf16 bits, ``[T][128]``."""
+    x = bf16_to_f64(index_k)                                   # [T][128]
+    wv = bf16_to_f64(w)
+    y = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + np.float64(eps)) * wv[None, :]
+    cs = np.asarray(cos_sin, dtype=np.float64)[np.asarray(positions, dtype=np.int64)]
+    c, s = cs[:, :D_ROPE // 2], cs[:, D_ROPE // 2:]
+    nope = D_INDEX - D_ROPE
+    x1, x2 = y[:, nope::2], y[:, nope + 1::2]
+    out = y.copy()
+    out[:, nope::2] = x1 * c - x2 * s
+    out[:, nope + 1::2] = x2 * c + x1 * s
+    return f64_to_bf16(out)
+
+
+def index_cache_insert(cache, slot_mapping, index_k_out, scale):
+    """Write the materialised indexer keys into a copy of the fp8 indexer
+    cache ``[...][128]`` at their slots (slots < 0 are skipped)."""
+    out = cache.copy()
+    flat = out.reshape(-1, D_INDEX)
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        flat[slot] = f64_to_e4m3(bf16_to_f64(index_k_out[t]) / np.float64(scale))
     return out
