@@ -72,6 +72,7 @@ class Spec:
     q_pos_step: int = 1             # causal: row i ends at 1 + i*step
     q_len: int = 1                  # query tokens per request (multi-token decode)
     pcp: int = 0                    # >0: prologue in sequence-sharded (PCP) form over pcp ranks
+    indexer: bool = False           # prologue also runs the indexer-key branch
 
 
 CONFIGS = {
@@ -132,6 +133,14 @@ PARITY_CASES = {
     # the most shards the library takes: 16 shards of interleave 2
     "s16_s": Spec("s16_s", rows=3, ctx=12007, shards=16, interleave=2, k=512,
                   heads=16, seed=21, row_ends="mixed"),
+    # the prologue's indexer-key branch in the same launch: materialised and
+    # inserted into an fp8 indexer cache (decode), materialised only
+    # (sequence-sharded prologue over 2 ranks)
+    "idx_s": Spec("idx_s", rows=5, ctx=5000, shards=2, interleave=1, k=512,
+                  heads=16, seed=23, cache="fp8", prologue=True, indexer=True,
+                  row_ends="mixed"),
+    "idx_pcp_s": Spec("idx_pcp_s", rows=4, ctx=3000, shards=1, interleave=1, k=512,
+                      heads=16, seed=24, cache="fp8", prologue=True, indexer=True, pcp=2),
 }
 
 
@@ -243,6 +252,12 @@ class Case:
     cos_sin: Optional[np.ndarray] = None     # [n_pos][64] float32: cos | sin
     positions: Optional[np.ndarray] = None   # [T] int32
     slot_mapping: Optional[np.ndarray] = None  # [T] int64
+    # indexer-key branch of the prologue, present when spec.indexer
+    index_k: Optional[np.ndarray] = None       # [T][128] uint16 (bf16)
+    index_w: Optional[np.ndarray] = None       # [128] uint16 (bf16)
+    index_eps: float = 1e-6
+    index_cache: Optional[np.ndarray] = None   # [nblocks][64][128] uint8 (e4m3)
+    index_scale: np.float32 = np.float32(2.0 ** -4)
 
     # convenience views
     @property
@@ -392,6 +407,12 @@ def make(name_or_spec, *, with_cache: bool = True) -> Case:
             blk = block_table[sh, row_req[t], loc // BLOCK]
             slots[t] = int(blk) * BLOCK + int(loc % BLOCK)
         case.slot_mapping = slots
+        if sp.indexer:
+            # drawn after every other input, so the other cases keep their data
+            case.index_k = _draw_bf16_normal(rng, (T, 128), 1.0)
+            case.index_w = _f64_to_bf16_bits(rng.uniform(0.5, 1.5, size=128))
+            case.index_cache = _draw_fp8_normal(rng, (nblocks, BLOCK, 128), 1.0 / sp.fp8_scale)
+            case.index_scale = np.float32(sp.fp8_scale)
     return case
 
 
@@ -425,6 +446,13 @@ def device_arrays(case: Case, device="cuda", logits=None, q=None) -> dict:
         d["prologue"] = dict(kv_c=bf16(case.kv_c), k_pe=bf16(case.k_pe), rms_w=bf16(case.rms_w),
                              eps=float(case.rms_eps), cos_sin=dev(case.cos_sin),
                              positions=dev(case.positions), slot_mapping=dev(case.slot_mapping))
+        if sp.indexer:
+            d["prologue"].update(
+                index_k=bf16(case.index_k), index_w=bf16(case.index_w),
+                index_eps=float(case.index_eps),
+                index_cache=None if sp.pcp else dev(case.index_cache),
+                index_cache_scale=None if sp.pcp else dev(np.array([case.index_scale],
+                                                                   dtype=np.float32)))
         if sp.pcp:
             d["pcp_ranks"] = sp.pcp
     return d

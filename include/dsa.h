@@ -63,6 +63,7 @@ typedef enum { DSA_BF16 = 1, DSA_FP32 = 2, DSA_FP8_E4M3 = 3 } dsa_dtype;
 #define DSA_LATENT_DIM 576  /* 512 kv_c + 64 rope */
 #define DSA_VALUE_DIM 512
 #define DSA_ROPE_DIM 64
+#define DSA_INDEX_DIM 128   /* indexer key: 64 unrotated + 64 rotary dimensions */
 #define DSA_MAX_SHARDS 16
 #define DSA_MAX_ID (1 << 24) /* global ids travel as exact fp32 values */
 
@@ -238,27 +239,48 @@ int dsa_lse_combine(const void* part_out, const float* part_lse,
 
 /*
  * dsa_fused_rmsnorm_rope — RMSNorm over kv_c + interleaved-pair RoPE over
- * k_pe; materialise and/or insert into the latent cache.
+ * k_pe (the latent branch), and the same for the indexer key (the indexer
+ * branch); each branch materialises and/or inserts into its cache.
  *
- * Source: [C] 实现拆解 item 1 and 关键源码片段 (`_fused_norm_rope_kernel`,
- * branch pid == 1): y = RMSNorm(kv_c) with weight w and epsilon; for pair i,
- * (x1, x2) = (k_pe[2i], k_pe[2i+1]), r1 = x1*cos - x2*sin, r2 = x2*cos +
- * x1*sin, stored back interleaved; outputs are materialised when their
+ * Source: [C] 实现拆解 item 1 and 关键源码片段 (`_fused_norm_rope_kernel`).
+ * Latent branch (pid == 1): y = RMSNorm(kv_c) with weight w and epsilon; for
+ * pair i, (x1, x2) = (k_pe[2i], k_pe[2i+1]), r1 = x1*cos - x2*sin, r2 = x2*cos
+ * + x1*sin, stored back interleaved; the outputs are materialised when their
  * pointers are given, and the cache entry [y | r] is written at the slot when
- * a slot mapping is given (fp8: value / scale cast to e4m3).  The call returns
- * early only when both outputs and the slot mapping are NULL.
+ * a slot mapping and a cache are given (fp8: value / scale cast to e4m3).
+ * Indexer branch (pid == 0): the indexer key is materialised into
+ * index_k_out when given, and quantised to fp8 and written into the indexer
+ * cache only when both index_cache and slot_mapping are given.  The call
+ * returns at once, with nothing written, only when all three outputs
+ * (kv_c_out, k_pe_out, index_k_out) and the slot mapping are NULL.
+ *
+ * The pages do not print the indexer branch's arithmetic; this library takes
+ * the plainest reading of the latent branch: the key is 128 wide (64
+ * unrotated dimensions, then a 64-dimension rotary part), RMSNorm over all
+ * 128 with weight index_w and index_eps, then the same interleaved-pair RoPE
+ * over the last 64 (same table and position), rounded once to bf16; the
+ * indexer cache holds e4m3(bf16 value / *index_cache_scale) (nearest-even,
+ * saturating at 448), 128 bytes per slot, at the latent branch's slots.
  *
  * kv_c [T][kv_c_ld] bf16 (first 512 used); k_pe [T][k_pe_ld] bf16 (first 64);
  * rms_w [512] bf16; cos_sin [n_pos][64] fp32 = cos(32) | sin(32) of each
  * position; positions [T] int32 (rows with a position outside [0, n_pos)
- * are left unwritten).
+ * are left unwritten by both branches).
  * kv_c_out [T][512], k_pe_out [T][64] bf16 outputs (each NULL: not written).
  * cache [num_slots][576] bf16 or fp8 e4m3; cache_scale device fp32 scalar
  * (fp8); slot_mapping [T] int64 (NULL: no insert; entries < 0 or >=
  * num_slots are skipped).  Inserted values are the materialised bf16
  * values (fp8: e4m3(bf16 value / scale), nearest-even, saturating at 448).
- * Errors: INVALID_ARG (null required pointers, T < 0, lds < widths),
- * UNSUPPORTED_DTYPE (cache not bf16/fp8 when inserting).
+ * index_k [T][index_k_ld] bf16 (first 128 used); index_w [128] bf16;
+ * index_k_out [T][128] bf16 output (NULL: not written); index_cache
+ * [index_num_slots][128] e4m3 (NULL: no indexer insert); index_cache_scale
+ * device fp32 scalar.  The inputs of a branch are read only when it writes
+ * something (the latent branch: kv_c_out, k_pe_out or a cache insert; the
+ * indexer branch: index_k_out or an indexer-cache insert); both run in one
+ * launch.
+ * Errors: INVALID_ARG (a branch's null inputs, a slot mapping without any
+ * cache, T < 0, lds < widths, misaligned pointers, missing scales),
+ * UNSUPPORTED_DTYPE (latent cache not bf16/fp8 when inserting).
  */
 int dsa_fused_rmsnorm_rope(const void* kv_c, int64_t kv_c_ld, const void* k_pe,
                            int64_t k_pe_ld, int32_t T, const void* rms_w,
@@ -267,7 +289,11 @@ int dsa_fused_rmsnorm_rope(const void* kv_c, int64_t kv_c_ld, const void* k_pe,
                            void* k_pe_out, void* cache, int32_t cache_dtype,
                            const float* cache_scale,
                            const int64_t* slot_mapping, int64_t num_slots,
-                           hipStream_t stream);
+                           const void* index_k, int64_t index_k_ld,
+                           const void* index_w, float index_eps,
+                           void* index_k_out, void* index_cache,
+                           const float* index_cache_scale,
+                           int64_t index_num_slots, hipStream_t stream);
 
 /*
  * dsa_cache_insert — write already materialised K rows into the latent cache.

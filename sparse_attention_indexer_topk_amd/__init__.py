@@ -45,7 +45,7 @@ SIGNATURES = {
                               _P, _P, _P],
     "dsa_lse_combine": [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
     "dsa_fused_rmsnorm_rope": [_P, _I64, _P, _I64, _I32, _P, _F32, _P, _I32, _P, _P, _P, _P, _I32, _P,
-                               _P, _I64, _P],
+                               _P, _I64, _P, _I64, _P, _F32, _P, _P, _P, _I64, _P],
     "dsa_cache_insert": [_P, _I64, _P, _I64, _I32, _P, _I32, _P, _P, _I64, _P],
     "dsa_last_error": [],
     "dsa_version": [],
@@ -411,43 +411,86 @@ def _check_rows_in(kv_c, k_pe):
     return kv_c.shape[0]
 
 
-def fused_rmsnorm_rope(kv_c: torch.Tensor, k_pe: torch.Tensor, rms_w: torch.Tensor, eps: float,
-                       cos_sin: torch.Tensor, positions: torch.Tensor, *,
+def fused_rmsnorm_rope(kv_c: Optional[torch.Tensor], k_pe: Optional[torch.Tensor],
+                       rms_w: Optional[torch.Tensor], eps: float, cos_sin: torch.Tensor,
+                       positions: torch.Tensor, *,
                        kv_c_out: Optional[torch.Tensor] = None,
                        k_pe_out: Optional[torch.Tensor] = None,
                        cache: Optional[torch.Tensor] = None,
                        cache_scale: Optional[torch.Tensor] = None,
-                       slot_mapping: Optional[torch.Tensor] = None, stream=None):
-    """RMSNorm(kv_c) + RoPE(k_pe); writes the given outputs and/or inserts into
-    ``cache`` at ``slot_mapping``.  Returns (kv_c_out, k_pe_out)."""
-    T = _check_rows_in(kv_c, k_pe)
-    _bits16(rms_w, "rms_w")
-    _shape(rms_w, "rms_w", (512,))
-    _contig(rms_w, "rms_w")
+                       slot_mapping: Optional[torch.Tensor] = None,
+                       index_k: Optional[torch.Tensor] = None,
+                       index_w: Optional[torch.Tensor] = None, index_eps: float = 1e-6,
+                       index_k_out: Optional[torch.Tensor] = None,
+                       index_cache: Optional[torch.Tensor] = None,
+                       index_cache_scale: Optional[torch.Tensor] = None, stream=None):
+    """Latent branch: RMSNorm(kv_c) + RoPE(k_pe), materialised into the given
+    outputs and/or inserted into ``cache`` at ``slot_mapping``.  Indexer
+    branch: the 128-wide indexer key normed and roped, materialised into
+    ``index_k_out`` and/or inserted into the fp8 ``index_cache`` (only with a
+    slot mapping).  Returns (kv_c_out, k_pe_out, index_k_out)."""
     _need(cos_sin, "cos_sin", torch.float32)
     _shape(cos_sin, "cos_sin", (None, 64))
     _contig(cos_sin, "cos_sin")
-    _check_row_vec(positions, "positions", T)
-    for name, t, w in (("kv_c_out", kv_c_out, 512), ("k_pe_out", k_pe_out, 64)):
+    _need(positions, "positions", torch.int32)
+    if positions.dim() != 1:
+        raise RuntimeError("positions must be [T]")
+    _contig(positions, "positions")
+    T = positions.shape[0]
+    latent = (kv_c_out is not None or k_pe_out is not None
+              or (slot_mapping is not None and cache is not None))
+    indexer = index_k_out is not None or (slot_mapping is not None and index_cache is not None)
+    if slot_mapping is not None:
+        _check_row_vec(slot_mapping, "slot_mapping", T, torch.int64)
+        if cache is None and index_cache is None:
+            raise RuntimeError("slot_mapping needs a cache")
+    if latent:
+        if _check_rows_in(kv_c, k_pe) != T:
+            raise RuntimeError(f"kv_c has {kv_c.shape[0]} rows, positions {T}")
+        _bits16(rms_w, "rms_w")
+        _shape(rms_w, "rms_w", (512,))
+        _contig(rms_w, "rms_w")
+    for name, t, w in (("kv_c_out", kv_c_out, 512), ("k_pe_out", k_pe_out, 64),
+                       ("index_k_out", index_k_out, 128)):
         if t is not None:
             _bits16(t, name)
             _shape(t, name, (T, w))
             _contig(t, name)
     cdt, num_slots = 0, 0
-    if slot_mapping is not None:
-        _check_row_vec(slot_mapping, "slot_mapping", T, torch.int64)
-        if cache is None:
-            raise RuntimeError("slot_mapping needs a cache")
+    if slot_mapping is not None and cache is not None:
         cdt = _check_cache(cache)
         _check_scale(cache_scale, cdt)
         num_slots = cache.numel() // 576
-    _same_device(kv_c, k_pe, rms_w, cos_sin, positions, kv_c_out, k_pe_out, cache, cache_scale,
-                 slot_mapping)
+    index_ld, index_slots = 0, 0
+    if indexer:
+        _bits16(index_k, "index_k")
+        if index_k.dim() != 2 or index_k.shape[0] != T or index_k.shape[1] < 128:
+            raise RuntimeError(f"index_k must be [T][>=128] (got {list(index_k.shape)})")
+        _row_major(index_k, "index_k")
+        index_ld = index_k.stride(0)
+        _bits16(index_w, "index_w")
+        _shape(index_w, "index_w", (128,))
+        _contig(index_w, "index_w")
+    if slot_mapping is not None and index_cache is not None:
+        _need(index_cache, "index_cache")
+        if index_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or index_cache.shape[-1] != 128:
+            raise RuntimeError("index_cache must hold 128 fp8 e4m3 codes per slot")
+        _contig(index_cache, "index_cache")
+        _check_scale(index_cache_scale, DSA_FP8_E4M3)
+        index_slots = index_cache.numel() // 128
+    _same_device(kv_c if latent else None, k_pe if latent else None, rms_w if latent else None,
+                 cos_sin, positions, kv_c_out, k_pe_out, cache, cache_scale, slot_mapping,
+                 index_k if indexer else None, index_w if indexer else None, index_k_out,
+                 index_cache, index_cache_scale)
     _check(lib().dsa_fused_rmsnorm_rope(
-        _ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), T, _ptr(rms_w), float(eps),
-        _ptr(cos_sin), cos_sin.shape[0], _ptr(positions), _ptr(kv_c_out), _ptr(k_pe_out),
-        _ptr(cache), cdt, _ptr(cache_scale), _ptr(slot_mapping), num_slots, _stream(stream)))
-    return kv_c_out, k_pe_out
+        _ptr(kv_c) if latent else None, kv_c.stride(0) if latent else 0,
+        _ptr(k_pe) if latent else None, k_pe.stride(0) if latent else 0, T,
+        _ptr(rms_w) if latent else None, float(eps), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(positions), _ptr(kv_c_out), _ptr(k_pe_out), _ptr(cache), cdt, _ptr(cache_scale),
+        _ptr(slot_mapping), num_slots, _ptr(index_k) if indexer else None, index_ld,
+        _ptr(index_w) if indexer else None, float(index_eps), _ptr(index_k_out),
+        _ptr(index_cache), _ptr(index_cache_scale), index_slots, _stream(stream)))
+    return kv_c_out, k_pe_out, index_k_out
 
 
 def cache_insert(kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,

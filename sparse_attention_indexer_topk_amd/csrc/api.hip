@@ -203,37 +203,73 @@ int dsa_fused_rmsnorm_rope(const void* kv_c, int64_t kv_c_ld, const void* k_pe, 
                            int32_t n_pos, const int32_t* positions, void* kv_c_out,
                            void* k_pe_out, void* cache, int32_t cache_dtype,
                            const float* cache_scale, const int64_t* slot_mapping,
-                           int64_t num_slots, hipStream_t stream) {
+                           int64_t num_slots, const void* index_k, int64_t index_k_ld,
+                           const void* index_w, float index_eps, void* index_k_out,
+                           void* index_cache, const float* index_cache_scale,
+                           int64_t index_num_slots, hipStream_t stream) {
   const char* fn = "dsa_fused_rmsnorm_rope";
   if (T < 0) return fail(DSA_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
-  if (!kv_c_out && !k_pe_out && !slot_mapping) return DSA_OK;  // nothing to produce
-  if (!kv_c || !k_pe || !rms_w || !cos_sin || !positions)
-    return fail(DSA_ERR_INVALID_ARG, "%s: NULL input pointer", fn);
-  if (kv_c_ld < DSA_VALUE_DIM || kv_c_ld % 8 != 0)
-    return fail(DSA_ERR_INVALID_ARG, "%s: kv_c_ld=%lld must be >= 512 and a multiple of 8", fn,
-                (long long)kv_c_ld);
-  if (k_pe_ld < DSA_ROPE_DIM || k_pe_ld % 2 != 0)
-    return fail(DSA_ERR_INVALID_ARG, "%s: k_pe_ld=%lld must be >= 64 and even", fn,
-                (long long)k_pe_ld);
+  // the early return of the profiling path: every output NULL and no slot
+  // mapping, so nothing is materialised or inserted
+  if (!kv_c_out && !k_pe_out && !index_k_out && !slot_mapping) return DSA_OK;
+  if (slot_mapping && !cache && !index_cache)
+    return fail(DSA_ERR_INVALID_ARG, "%s: slot_mapping without a cache", fn);
+  const bool latent = kv_c_out || k_pe_out || (slot_mapping && cache);
+  const bool indexer = index_k_out || (slot_mapping && index_cache);
+  if (!cos_sin || !positions) return fail(DSA_ERR_INVALID_ARG, "%s: NULL cos_sin/positions", fn);
   if (n_pos < 1) return fail(DSA_ERR_INVALID_ARG, "%s: n_pos=%d < 1", fn, n_pos);
   int kind = 0;
-  if (slot_mapping) {
-    if (!cache) return fail(DSA_ERR_INVALID_ARG, "%s: slot_mapping without cache", fn);
-    if (cache_dtype == DSA_BF16) kind = 1;
-    else if (cache_dtype == DSA_FP8_E4M3) kind = 2;
-    else return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: cache dtype %d is not bf16 or fp8", fn,
-                     cache_dtype);
-    if (kind == 2 && !cache_scale) return fail(DSA_ERR_INVALID_ARG, "%s: fp8 cache needs cache_scale", fn);
-    if (num_slots < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_slots < 0", fn);
+  if (latent) {
+    if (!kv_c || !k_pe || !rms_w) return fail(DSA_ERR_INVALID_ARG, "%s: NULL input pointer", fn);
+    if (kv_c_ld < DSA_VALUE_DIM || kv_c_ld % 8 != 0)
+      return fail(DSA_ERR_INVALID_ARG, "%s: kv_c_ld=%lld must be >= 512 and a multiple of 8", fn,
+                  (long long)kv_c_ld);
+    if (k_pe_ld < DSA_ROPE_DIM || k_pe_ld % 2 != 0)
+      return fail(DSA_ERR_INVALID_ARG, "%s: k_pe_ld=%lld must be >= 64 and even", fn,
+                  (long long)k_pe_ld);
+    if (slot_mapping && cache) {
+      if (cache_dtype == DSA_BF16) kind = 1;
+      else if (cache_dtype == DSA_FP8_E4M3) kind = 2;
+      else return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: cache dtype %d is not bf16 or fp8", fn,
+                       cache_dtype);
+      if (kind == 2 && !cache_scale)
+        return fail(DSA_ERR_INVALID_ARG, "%s: fp8 cache needs cache_scale", fn);
+      if (num_slots < 0) return fail(DSA_ERR_INVALID_ARG, "%s: num_slots < 0", fn);
+    }
+  }
+  if (indexer) {
+    if (!index_k || !index_w)
+      return fail(DSA_ERR_INVALID_ARG, "%s: NULL index_k/index_w", fn);
+    if (index_k_ld < DSA_INDEX_DIM || index_k_ld % 2 != 0)
+      return fail(DSA_ERR_INVALID_ARG, "%s: index_k_ld=%lld must be >= 128 and even", fn,
+                  (long long)index_k_ld);
+    if (slot_mapping && index_cache) {
+      if (!index_cache_scale)
+        return fail(DSA_ERR_INVALID_ARG, "%s: the fp8 indexer cache needs its scale", fn);
+      if (index_num_slots < 0) return fail(DSA_ERR_INVALID_ARG, "%s: index_num_slots < 0", fn);
+    }
   }
   if (!aligned(kv_c, 16) || !aligned(k_pe, 4) || !aligned(rms_w, 16) || !aligned(kv_c_out, 16) ||
       !aligned(k_pe_out, 4) || !aligned(cache, 16) || !aligned(cos_sin, 4) ||
-      !aligned(positions, 4) || !aligned(slot_mapping, 8))
+      !aligned(positions, 4) || !aligned(slot_mapping, 8) || !aligned(index_k, 4) ||
+      !aligned(index_w, 4) || !aligned(index_k_out, 4) || !aligned(index_cache, 2) ||
+      !aligned(index_cache_scale, 4))
     return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-  if (T == 0) return DSA_OK;
+  if (T == 0 || (!latent && !indexer)) return DSA_OK;
+  dsa::IndexerArgs ix{};
+  if (indexer) {
+    ix.k = reinterpret_cast<const uint16_t*>(index_k);
+    ix.ld = index_k_ld;
+    ix.w = reinterpret_cast<const uint16_t*>(index_w);
+    ix.eps = index_eps;
+    ix.out = reinterpret_cast<uint16_t*>(index_k_out);
+    ix.cache = slot_mapping ? reinterpret_cast<uint8_t*>(index_cache) : nullptr;
+    ix.scale = index_cache_scale;
+    ix.num_slots = index_num_slots;
+  }
   dsa::launch_fused_rmsnorm_rope(kv_c, kv_c_ld, k_pe, k_pe_ld, T, rms_w, eps, cos_sin, n_pos,
                                  positions, kv_c_out, k_pe_out, cache, kind, cache_scale,
-                                 slot_mapping, num_slots, stream);
+                                 slot_mapping, num_slots, latent, ix, indexer, stream);
   return launched(fn);
 }
 

@@ -13,6 +13,15 @@
 // load) and lanes 0..31 one rope pair; the sum of squares is a wave
 // butterfly; math in fp32; stores are 16 bytes (bf16) / 8 bytes (fp8).
 //
+// The indexer-key branch (the same kernel's pid == 0 branch: PR #52046
+// report, 实现拆解 item 1) runs in the same launch, one wave per token on the
+// second grid row: RMSNorm over the 128-wide key with its own weight, RoPE
+// over its last 64 dimensions in interleaved pairs (same table and position
+// as the latent branch), materialised when index_k_out is given, and written
+// into the fp8 indexer cache (e4m3(bf16 value / scale)) only when both that
+// cache and the slot mapping are given.  Each lane holds 2 elements; lanes
+// 32..63 hold the rotary pairs.
+//
 // cache_insert_kernel writes already materialised rows (the K rows that the
 // sequence-sharded (PCP) path gathers from every rank before the update of
 // its replicated cache: PR #52046 report, 关键源码片段, `do_kv_cache_update`
@@ -23,6 +32,7 @@
 namespace dsa {
 
 constexpr int kNormThreads = 256;  // 4 tokens per block
+constexpr int kIndexDim = 128;     // indexer key width
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -60,7 +70,43 @@ __device__ __forceinline__ void insert_row(int lane, const uint16_t (&y)[8], uin
   }
 }
 
-// CACHE: 0 = no insert, 1 = bf16 cache, 2 = fp8 e4m3 cache
+// The indexer-key row of token t at position pos (see the header comment).
+__device__ __forceinline__ void index_row(int t, int pos, int lane, const IndexerArgs& ix,
+                                          const float* __restrict__ cos_sin,
+                                          const int64_t* __restrict__ slot_mapping) {
+  const uint32_t xv = *reinterpret_cast<const uint32_t*>(ix.k + (int64_t)t * ix.ld + 2 * lane);
+  const uint32_t wv = *reinterpret_cast<const uint32_t*>(ix.w + 2 * lane);
+  const float x0 = bf16_to_f32((uint16_t)(xv & 0xffffu));
+  const float x1 = bf16_to_f32((uint16_t)(xv >> 16));
+  const float ss = wave_sum(x0 * x0 + x1 * x1);
+  const float inv_rms = 1.0f / sqrtf(ss / (float)kIndexDim + ix.eps);
+  float y0 = x0 * inv_rms * bf16_to_f32((uint16_t)(wv & 0xffffu));
+  float y1 = x1 * inv_rms * bf16_to_f32((uint16_t)(wv >> 16));
+  if (lane >= (kIndexDim - kRope) / 2) {   // rotary pair i = lane - 32
+    const int i = lane - (kIndexDim - kRope) / 2;
+    const float c = cos_sin[(int64_t)pos * kRope + i];
+    const float s = cos_sin[(int64_t)pos * kRope + kRope / 2 + i];
+    const float r0 = y0 * c - y1 * s;
+    const float r1 = y1 * c + y0 * s;
+    y0 = r0;
+    y1 = r1;
+  }
+  const uint16_t b0 = f32_to_bf16(y0), b1 = f32_to_bf16(y1);
+  if (ix.out)
+    *reinterpret_cast<uint32_t*>(ix.out + (int64_t)t * kIndexDim + 2 * lane) =
+        (uint32_t)b0 | ((uint32_t)b1 << 16);
+  if (ix.cache && slot_mapping) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= ix.num_slots) return;
+    const float sc = ix.scale[0];
+    const uint32_t c0 = f32_to_e4m3(bf16_to_f32(b0) / sc);
+    const uint32_t c1 = f32_to_e4m3(bf16_to_f32(b1) / sc);
+    *reinterpret_cast<uint16_t*>(ix.cache + slot * kIndexDim + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  }
+}
+
+// CACHE: 0 = no insert, 1 = bf16 cache, 2 = fp8 e4m3 cache (latent branch).
+// Grid row blockIdx.y + role0: 0 = latent branch, 1 = indexer-key branch.
 template <int CACHE>
 __global__ __launch_bounds__(kNormThreads) void fused_rmsnorm_rope_kernel(
     const uint16_t* __restrict__ kv_c, int64_t kv_ld, const uint16_t* __restrict__ k_pe,
@@ -68,12 +114,16 @@ __global__ __launch_bounds__(kNormThreads) void fused_rmsnorm_rope_kernel(
     const float* __restrict__ cos_sin, int n_pos, const int* __restrict__ positions,
     uint16_t* __restrict__ kv_out, uint16_t* __restrict__ pe_out, void* __restrict__ cache,
     const float* __restrict__ cache_scale, const int64_t* __restrict__ slot_mapping,
-    int64_t num_slots) {
+    int64_t num_slots, IndexerArgs ix, int role0) {
   const int t = blockIdx.x * (kNormThreads / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // per-wave early out; no block barriers below
   const int lane = lane_id();
   const int pos = positions[t];
   if (pos < 0 || pos >= n_pos) return;
+  if (role0 + (int)blockIdx.y == 1) {
+    index_row(t, pos, lane, ix, cos_sin, slot_mapping);
+    return;
+  }
 
   // RMSNorm over 512
   const uint4 xv = *reinterpret_cast<const uint4*>(kv_c + (int64_t)t * kv_ld + 8 * lane);
@@ -166,10 +216,12 @@ int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe,
                               int T, const void* w, float eps, const float* cos_sin, int n_pos,
                               const int* positions, void* kv_out, void* pe_out, void* cache,
                               int cache_kind, const float* cache_scale,
-                              const int64_t* slot_mapping, int64_t num_slots,
-                              hipStream_t stream) {
+                              const int64_t* slot_mapping, int64_t num_slots, bool latent,
+                              const IndexerArgs& ix, bool indexer, hipStream_t stream) {
   const int wpb = kNormThreads / kWave;
-  dim3 grid((T + wpb - 1) / wpb);
+  // grid rows: the latent branch and/or the indexer-key branch
+  const int role0 = latent ? 0 : 1;
+  dim3 grid((T + wpb - 1) / wpb, (latent ? 1 : 0) + (indexer ? 1 : 0));
   auto a0 = reinterpret_cast<const uint16_t*>(kv_c);
   auto a1 = reinterpret_cast<const uint16_t*>(k_pe);
   auto a2 = reinterpret_cast<const uint16_t*>(w);
@@ -178,7 +230,7 @@ int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe,
 #define DSA_LAUNCH_NORM(C)                                                                   \
   hipLaunchKernelGGL(fused_rmsnorm_rope_kernel<C>, grid, dim3(kNormThreads), 0, stream, a0,  \
                      kv_ld, a1, pe_ld, T, a2, eps, cos_sin, n_pos, positions, o0, o1, cache, \
-                     cache_scale, slot_mapping, num_slots)
+                     cache_scale, slot_mapping, num_slots, ix, role0)
   if (cache_kind == 0) DSA_LAUNCH_NORM(0);
   else if (cache_kind == 1) DSA_LAUNCH_NORM(1);
   else DSA_LAUNCH_NORM(2);

@@ -35,11 +35,24 @@ int launch_cache_insert(const void* kv_c, int64_t kv_ld, const void* k_pe, int64
                         void* cache, int cache_kind, const float* cache_scale,
                         const int64_t* slot_mapping, int64_t num_slots, hipStream_t stream);
 
+// Indexer-key branch of the fused norm + RoPE launch (fields unused when the
+// branch does not run).
+struct IndexerArgs {
+  const uint16_t* k;     // [T][ld] bf16, first 128 used
+  int64_t ld;
+  const uint16_t* w;     // [128] bf16
+  float eps;
+  uint16_t* out;         // [T][128] bf16 (nullable)
+  uint8_t* cache;        // [num_slots][128] e4m3 (nullable)
+  const float* scale;    // device scalar (with cache)
+  int64_t num_slots;
+};
+
 int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld,
                               int T, const void* w, float eps, const float* cos_sin, int n_pos,
                               const int* positions, void* kv_out, void* pe_out, void* cache,
                               int cache_kind, const float* cache_scale,
-                              const int64_t* slot_mapping, int64_t num_slots,
-                              hipStream_t stream);
+                              const int64_t* slot_mapping, int64_t num_slots, bool latent,
+                              const IndexerArgs& ix, bool indexer, hipStream_t stream);
 
 }  // namespace dsa

@@ -34,6 +34,12 @@ class Prologue:
     cos_sin: torch.Tensor       # [n_pos][64] fp32
     positions: torch.Tensor     # [T] int32
     slot_mapping: torch.Tensor  # [T] int64
+    # indexer-key branch of the same launch (all None: not run)
+    index_k: Optional[torch.Tensor] = None            # [T][128] bf16
+    index_w: Optional[torch.Tensor] = None            # [128] bf16
+    index_eps: float = 1e-6
+    index_cache: Optional[torch.Tensor] = None        # [slots][128] fp8 e4m3 codes
+    index_cache_scale: Optional[torch.Tensor] = None  # [1] fp32
 
 
 class DecodePath:
@@ -75,27 +81,41 @@ class DecodePath:
         self.plse = torch.empty((S * splits, R, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((R, H, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+        self.index_k_out = None
         if prologue is not None:
             T = prologue.kv_c.shape[0]
             self.kv_c_out = torch.empty((T, 512), dtype=torch.bfloat16, device=dev)
             self.k_pe_out = torch.empty((T, 64), dtype=torch.bfloat16, device=dev)
+            if prologue.index_k is not None:
+                self.index_k_out = torch.empty((T, 128), dtype=torch.bfloat16, device=dev)
 
     # -- steps ---------------------------------------------------------------
     def run_prologue(self, stream=None):
         p = self.prologue
+        ix = p.index_k is not None
         if self.pcp_ranks <= 0:
             fused_rmsnorm_rope(p.kv_c, p.k_pe, p.rms_w, p.eps, p.cos_sin, p.positions,
                                kv_c_out=self.kv_c_out, k_pe_out=self.k_pe_out,
                                cache=self.cache, cache_scale=self.cache_scale,
-                               slot_mapping=p.slot_mapping, stream=stream)
+                               slot_mapping=p.slot_mapping, index_k=p.index_k,
+                               index_w=p.index_w, index_eps=p.index_eps,
+                               index_k_out=self.index_k_out, index_cache=p.index_cache,
+                               index_cache_scale=p.index_cache_scale, stream=stream)
             return
+        # sequence-sharded: every rank materialises its rows (the indexer key
+        # too, with no indexer-cache insert: the indexer takes the materialised
+        # keys), the rows are gathered, and the replicated cache is updated
         T = p.kv_c.shape[0]
         bounds = [T * r // self.pcp_ranks for r in range(self.pcp_ranks + 1)]
         for a, b in zip(bounds[:-1], bounds[1:]):   # rank r materialises rows [a, b)
             if b > a:
                 fused_rmsnorm_rope(p.kv_c[a:b], p.k_pe[a:b], p.rms_w, p.eps, p.cos_sin,
                                    p.positions[a:b], kv_c_out=self.kv_c_out[a:b],
-                                   k_pe_out=self.k_pe_out[a:b], stream=stream)
+                                   k_pe_out=self.k_pe_out[a:b],
+                                   index_k=p.index_k[a:b] if ix else None, index_w=p.index_w,
+                                   index_eps=p.index_eps,
+                                   index_k_out=self.index_k_out[a:b] if ix else None,
+                                   stream=stream)
         cache_insert(self.kv_c_out, self.k_pe_out, self.cache, p.slot_mapping,
                      cache_scale=self.cache_scale, stream=stream)
 

@@ -139,13 +139,18 @@ def test_fused_rmsnorm_rope_rejects():
     f = L.dsa_fused_rmsnorm_rope
     def call(**kw):
         a = dict(kv=FAKE, kvld=512, pe=FAKE, peld=64, T=0, w=FAKE, eps=1e-6, cs=FAKE, npos=10,
-                 pos=FAKE, kvo=FAKE, peo=FAKE, cache=None, dt=0, scale=None, sm=None, nslots=0)
+                 pos=FAKE, kvo=FAKE, peo=FAKE, cache=None, dt=0, scale=None, sm=None, nslots=0,
+                 ik=None, ikld=0, iw=None, ieps=1e-6, iko=None, icache=None, iscale=None,
+                 inslots=0)
         a.update(kw)
         return f(a["kv"], a["kvld"], a["pe"], a["peld"], a["T"], a["w"], a["eps"], a["cs"],
                  a["npos"], a["pos"], a["kvo"], a["peo"], a["cache"], a["dt"], a["scale"], a["sm"],
-                 a["nslots"], None)
+                 a["nslots"], a["ik"], a["ikld"], a["iw"], a["ieps"], a["iko"], a["icache"],
+                 a["iscale"], a["inslots"], None)
     assert call() == OK
-    assert call(kvo=None, peo=None, T=5) == OK         # nothing to produce: early return
+    # nothing to produce (three outputs and the slot mapping NULL): early
+    # return, whatever the inputs are
+    assert call(kvo=None, peo=None, T=5, kv=None, cs=None) == OK
     assert call(kvld=500) == INV
     assert call(peld=63) == INV
     assert call(w=None) == INV
@@ -153,6 +158,20 @@ def test_fused_rmsnorm_rope_rejects():
     assert call(sm=FAKE, cache=FAKE, dt=dsa.DSA_FP32) == BADT
     assert call(sm=FAKE, cache=FAKE, dt=dsa.DSA_FP8_E4M3) == INV   # no scale
     assert call(T=-1) == INV
+    # indexer branch: runs when index_k_out is given, or an indexer cache and a
+    # slot mapping; then its inputs and the cache's scale are required
+    ik = dict(ik=FAKE, ikld=128, iw=FAKE, iko=FAKE)
+    assert call(**ik) == OK
+    assert call(kvo=None, peo=None, kv=None, pe=None, w=None, **ik) == OK   # indexer only
+    assert call(**{**ik, "ik": None}) == INV
+    assert call(**{**ik, "iw": None}) == INV
+    assert call(**{**ik, "ikld": 100}) == INV
+    assert call(**{**ik, "ikld": 129}) == INV
+    assert call(sm=FAKE, icache=FAKE, **ik) == INV                  # no indexer-cache scale
+    assert call(sm=FAKE, icache=FAKE, iscale=FAKE, inslots=64, **ik) == OK
+    # an indexer cache without a slot mapping is not written: the branch needs
+    # no inputs when index_k_out is NULL too
+    assert call(icache=FAKE, iscale=None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -55,7 +55,25 @@ def check_prologue(c, path):
     blank = np.zeros((T, 576), dtype=g_rows.dtype)
     exp_rows = oracle.cache_insert(blank, np.arange(T), kvo, peo, c.cache_dtype, c.cache_scale)
     assert np.array_equal(g_rows, exp_rows), "inserted cache bytes differ"
+    if c.spec.indexer:
+        check_indexer_branch(c, path)
     return oracle.cache_insert(blank, np.arange(T), okv, ope, c.cache_dtype, c.cache_scale)
+
+
+def check_indexer_branch(c, path):
+    """The prologue's indexer-key branch (run by path.run_prologue): keys
+    within 1 bf16 ulp of the oracle; with an indexer cache, the inserted bytes
+    are the oracle's quantisation of the GPU's own keys and no other slot
+    moved."""
+    gk = bits16(path.index_k_out)
+    ok = oracle.index_norm_rope(c.index_k, c.index_w, c.index_eps, c.cos_sin, c.positions)
+    assert bf16_ulp_diff(gk, ok).max() <= 1, "indexer keys differ"
+    icache = path.prologue.index_cache
+    if icache is None:          # sequence-sharded: keys materialised only
+        return
+    g = icache.cpu().numpy().reshape(-1, 128)
+    exp = oracle.index_cache_insert(c.index_cache, c.slot_mapping, gk, c.index_scale)
+    assert np.array_equal(g, exp.reshape(-1, 128)), "indexer cache bytes differ"
 
 
 def host_cache_after_insert(c, rows_oracle):
