@@ -49,6 +49,9 @@ def parse():
                    help="merge_candidates and convert_index as two launches")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="oracle time per CPU-baseline mode (single thread, all threads)")
+    p.add_argument("--launch-floor", action="store_true",
+                   help="only launch empty kernels with the grid shapes of the decode step's "
+                        "kernels (30 each), for a kernel trace of the launch floor")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (3 times), the reference "
                         "for scaling the HBM byte counters of a profile")
@@ -68,6 +71,22 @@ def calibrate_copy():
 
 
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache
+
+
+def launch_floor_grids():
+    """Empty launches with the grids of the decode workload's kernels (64 rows,
+    4 shards, 128 heads): top-K and merge_convert 256 x 1024 threads, the
+    attention 256 x 512, the combine 2048 x 256."""
+    import torch
+    import sparse_attention_indexer_topk_amd as dsa
+    grids = {"topk_select / merge_convert": (256, 1024), "sparse_mla_decode": (256, 512),
+             "lse_combine": (2048, 256)}
+    for _ in range(30):
+        for wg, nt in grids.values():
+            dsa.launch_floor(wg, nt)
+    torch.cuda.synchronize()
+    print(json.dumps({"launch_floor": {k: {"workgroups": v[0], "threads": v[1], "launches": 30}
+                                       for k, v in grids.items()}}), flush=True)
 
 
 def attention_traffic(c, counts_total):
@@ -178,6 +197,9 @@ def main():
     a = parse()
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.launch_floor:
+        launch_floor_grids()
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): every shard is emulated "

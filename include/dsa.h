@@ -320,6 +320,15 @@ int dsa_cache_insert(const void* kv_c, int64_t kv_c_ld, const void* k_pe,
                      const float* cache_scale, const int64_t* slot_mapping,
                      int64_t num_slots, hipStream_t stream);
 
+/*
+ * dsa_launch_floor — measurement helper, not a step of the path: launches a
+ * kernel that returns at once with `workgroups` workgroups of `threads`
+ * threads (256, 512 or 1024) on `stream`.  Its duration in a kernel trace is
+ * the floor a path kernel of the same grid shape pays before doing any work.
+ * Errors: INVALID_ARG (workgroups < 1, other thread counts).
+ */
+int dsa_launch_floor(int32_t workgroups, int32_t threads, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dsa_last_error(void);
 

@@ -47,6 +47,7 @@ SIGNATURES = {
     "dsa_fused_rmsnorm_rope": [_P, _I64, _P, _I64, _I32, _P, _F32, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                _P, _I64, _P, _I64, _P, _F32, _P, _P, _P, _I64, _P],
     "dsa_cache_insert": [_P, _I64, _P, _I64, _I32, _P, _I32, _P, _P, _I64, _P],
+    "dsa_launch_floor": [_I32, _I32, _P],
     "dsa_last_error": [],
     "dsa_version": [],
 }
@@ -138,6 +139,11 @@ def _same_device(*ts):
     devs = {t.device for t in ts if t is not None}
     if len(devs) > 1:
         raise RuntimeError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def launch_floor(workgroups: int, threads: int, stream=None):
+    """Launch an empty kernel of the given grid shape (a measurement helper)."""
+    _check(lib().dsa_launch_floor(int(workgroups), int(threads), _stream(stream)))
 
 
 def version() -> int:
@@ -510,4 +516,4 @@ def cache_insert(kv_c: torch.Tensor, k_pe: torch.Tensor, cache: torch.Tensor,
 
 __all__ = ["lib", "version", "DSAError", "topk_select", "merge_candidates", "convert_index",
            "merge_convert", "sparse_mla_decode", "lse_combine", "fused_rmsnorm_rope",
-           "cache_insert", "LIB_PATH", "SIGNATURES"]
+           "cache_insert", "launch_floor", "LIB_PATH", "SIGNATURES"]

@@ -301,4 +301,13 @@ int dsa_cache_insert(const void* kv_c, int64_t kv_c_ld, const void* k_pe, int64_
   return launched(fn);
 }
 
+int dsa_launch_floor(int32_t workgroups, int32_t threads, hipStream_t stream) {
+  const char* fn = "dsa_launch_floor";
+  if (workgroups < 1) return fail(DSA_ERR_INVALID_ARG, "%s: workgroups=%d < 1", fn, workgroups);
+  if (threads != 256 && threads != 512 && threads != 1024)
+    return fail(DSA_ERR_INVALID_ARG, "%s: threads=%d not 256, 512 or 1024", fn, threads);
+  dsa::launch_floor(workgroups, threads, stream);
+  return launched(fn);
+}
+
 }  // extern "C"

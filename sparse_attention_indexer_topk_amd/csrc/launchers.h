@@ -55,4 +55,6 @@ int launch_fused_rmsnorm_rope(const void* kv_c, int64_t kv_ld, const void* k_pe,
                               const int64_t* slot_mapping, int64_t num_slots, bool latent,
                               const IndexerArgs& ix, bool indexer, hipStream_t stream);
 
+int launch_floor(int workgroups, int threads, hipStream_t stream);
+
 }  // namespace dsa
