@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--pcp", type=int, default=0,
                    help="prologue in sequence-sharded form over this many ranks "
                         "(materialise per rank, gather, insert)")
+    p.add_argument("--no-merge-ids", action="store_true",
+                   help="merge_convert writes only the slot lists and counts, not the merged "
+                        "global ids (nothing downstream reads them)")
     p.add_argument("--unfused", action="store_true",
                    help="merge_candidates and convert_index as two launches")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -110,12 +113,13 @@ def attention_traffic(c, counts_total):
     return fixed + gathered, unique, flops
 
 
-def topk_traffic(c, n_valid_logits, fused=True):
+def topk_traffic(c, n_valid_logits, fused=True, ids=True):
     """Algorithmic bytes of topk_select and of the merge launch for one step
-    (merge_convert also writes the slot lists and counts)."""
+    (merge_convert also writes the slot lists and counts; ids=False: it does
+    not write the merged ids)."""
     R, S, k = c.rows, c.S, c.k
     topk = n_valid_logits * 4 + R * S * k * 8         # logits read, candidates written
-    merge = R * S * k * 8 + R * k * 4                 # candidates read, ids written
+    merge = R * S * k * 8 + (R * k * 4 if ids else 0)  # candidates read, ids written
     if fused:
         merge += S * R * k * 4 + S * R * 4            # slots and counts written
     return topk, merge
@@ -223,6 +227,7 @@ def main():
             sys.exit(2)
         arrays["pcp_ranks"] = a.pcp
     path = DecodePath(**arrays)
+    path.want_ids = a.unfused or not a.no_merge_ids
     logits_sets, q_sets = [path.logits], [path.q]
     for s in range(1, a.sets):
         lg, qq = dsa_inputs.redraw_logits_q(c, s)
@@ -306,7 +311,8 @@ def main():
     for i in range(c.rows):
         n_valid += int(c.row_ends[i]) - int(c.row_starts[i])
     att_bytes, att_unique, att_flops = attention_traffic(c, counts_total)
-    tk_bytes, mg_bytes = topk_traffic(c, n_valid, fused=not a.unfused)
+    tk_bytes, mg_bytes = topk_traffic(c, n_valid, fused=not a.unfused,
+                                      ids=a.unfused or not a.no_merge_ids)
     t_att = att_us * 1e-6
     att_tflops = att_flops / t_att / 1e12
     # the binding roof: HBM time of the bytes HBM must deliver vs MFMA time
@@ -342,7 +348,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": c.spec.name, "rows": c.rows, "ctx": c.ctx, "k": c.k,
                    "shards": c.S, "interleave": c.I, "heads": c.heads, "cache": c.cache_dtype,
-                   "input_sets": a.sets, **({"pcp_ranks": a.pcp} if a.pcp else {})},
+                   "input_sets": a.sets, "merged_ids_written": bool(path.want_ids),
+                   **({"pcp_ranks": a.pcp} if a.pcp else {})},
         "topk_rows_per_s": round(c.rows / t_topk, 1),
         "decode_tokens_per_s": round(c.rows / t_dec, 1),
         "sparse_mla_decode_us_timed": round(att_us, 2),

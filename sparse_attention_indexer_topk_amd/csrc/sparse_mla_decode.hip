@@ -232,7 +232,7 @@ __device__ __forceinline__ int lane_now() {
   return l;
 }
 
-template <bool FP8, bool OFF32>
+template <bool FP8, bool OFF32, bool FULL>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
     const float* __restrict__ cache_scale, int64_t num_slots, const int* __restrict__ slots,
@@ -269,8 +269,11 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   const int g4 = lane >> 4;       // k-group of the 16x16x32 operands
   const int h0 = hg * kHPB + wave * kHPW;
   const int head = h0 + n16;
-  const bool wave_on = h0 < heads;   // heads is a multiple of 16
-  const int n_hb = (heads - hg * kHPB) / 16 < kNHB ? (heads - hg * kHPB) / 16 : kNHB;
+  // FULL: every workgroup holds kHPB heads (heads a multiple of 128), so the
+  // head-block guards below fold away
+  const bool wave_on = FULL || h0 < heads;   // heads is a multiple of 16
+  const int n_hb = FULL ? kNHB
+                        : ((heads - hg * kHPB) / 16 < kNHB ? (heads - hg * kHPB) / 16 : kNHB);
   const int out_part = yz % gridDim.y;
   const int slot_lim = num_slots > 0x7fffffffLL ? 0x7fffffff : (int)num_slots;
 
@@ -634,12 +637,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
 
   // ---- epilogue ---------------------------------------------------------------
+  // the lane's indexes are rebuilt here rather than held across the loop
+  // (keeping them costs spill slots, and scratch costs every launch)
+  const int e_lane = lane_now();
+  const int e_n16 = e_lane & 15, e_g4 = e_lane >> 4;
   float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (wave_on && g4 == 0) {
-    s_inv[wave * kHPW + n16] = l_tot > 0.f ? kv_scale / l_tot : 0.f;
+  if (wave_on && e_g4 == 0) {
+    s_inv[wave * kHPW + e_n16] = l_tot > 0.f ? kv_scale / l_tot : 0.f;
     const float lv = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    lse[((int64_t)out_part * rows + row) * heads + head] = lv;
+    lse[((int64_t)out_part * rows + row) * heads + h0 + e_n16] = lv;
   }
   lgkm_wait0();
   bar();   // 1/l of every head published; every wave done with the ring
@@ -648,8 +655,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 #pragma unroll
   for (int hb = 0; hb < kNHB; ++hb) {
     if (hb < n_hb) {
-      const float inv = s_inv[16 * hb + n16];
-      uint8_t* stg = s_tiles + (16 * hb + n16) * kEpiRow + (64 * wave + 4 * g4) * 2;
+      const float inv = s_inv[16 * hb + e_n16];
+      uint8_t* stg = s_tiles + (16 * hb + e_n16) * kEpiRow + (64 * wave + 4 * e_g4) * 2;
 #pragma unroll
       for (int f = 0; f < kFBW; ++f) {
         const uint2 v = make_uint2(cvt_pk_bf16(o[f][hb][0] * inv, o[f][hb][1] * inv),
@@ -664,8 +671,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     uint16_t* ob = out + (((int64_t)out_part * rows + row) * heads + h0) * kValue;
 #pragma unroll
     for (int r = 0; r < kHPW; ++r) {
-      const uint4 v = *reinterpret_cast<const uint4*>(s_tiles + (wave * kHPW + r) * kEpiRow + lane * 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + lane * 16) = v;
+      const uint4 v = *reinterpret_cast<const uint4*>(s_tiles + (wave * kHPW + r) * kEpiRow + e_lane * 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ob + (int64_t)r * kValue) + e_lane * 16) = v;
     }
   }
 }
@@ -680,16 +687,22 @@ int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cac
   uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
   // 32-bit gather offsets when the whole pool lies within 4 GiB of its base
   const bool off32 = num_slots * (int64_t)(fp8 ? kRowB8 : kRowB) <= (int64_t)0xffffffffLL;
+  const bool full = heads % kHPB == 0;
 #define DSA_ATTN(F, O)                                                                       \
-  hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O>), grid, dim3(kAttnThreads), 0, stream,   \
-                     q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, splits,  \
-                     sm_scale, o16, lse)
+  if (full)                                                                                  \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, true>), grid, dim3(kAttnThreads), 0,   \
+                       stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, \
+                       splits, sm_scale, o16, lse);                                           \
+  else                                                                                       \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, false>), grid, dim3(kAttnThreads), 0,  \
+                       stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, \
+                       splits, sm_scale, o16, lse)
   if (fp8) {
-    if (off32) DSA_ATTN(true, true);
-    else DSA_ATTN(true, false);
+    if (off32) { DSA_ATTN(true, true); }
+    else { DSA_ATTN(true, false); }
   } else {
-    if (off32) DSA_ATTN(false, true);
-    else DSA_ATTN(false, false);
+    if (off32) { DSA_ATTN(false, true); }
+    else { DSA_ATTN(false, false); }
   }
 #undef DSA_ATTN
   return 0;

@@ -63,6 +63,9 @@ class DecodePath:
         # materialises its slice of the new K rows into the gathered buffer
         # (the all-gather, in place), then every row is inserted
         self.pcp_ranks = pcp_ranks
+        # the merged global ids are written out only when wanted: the
+        # per-shard slot lists the attention reads are derived without them
+        self.want_ids = True
         dev = logits.device
         R, H = q.shape[0], q.shape[1]
         S = num_shards
@@ -136,7 +139,8 @@ class DecodePath:
     def run_merge_convert(self, stream=None):
         merge_convert(self.cand, self.k, self.block_table, id_bound=self.ctx,
                       block_size=self.block_size, num_shards=self.S, interleave=self.I,
-                      row_req=self.row_req, ids=self.ids, slots=self.slots, counts=self.counts,
+                      row_req=self.row_req, ids=self.ids if self.want_ids else None,
+                      want_ids=self.want_ids, slots=self.slots, counts=self.counts,
                       stream=stream)
 
     def run_attention(self, stream=None, q=None):
