@@ -205,19 +205,23 @@ int dsa_merge_convert(const float* cand, int32_t rows, int32_t n_cand, int32_t k
  *              `splits` consecutive pieces (multiples of 32 slots), each
  *              producing its own partial; partial p*splits + s belongs to
  *              part p.  All partials merge with dsa_lse_combine.
- * out          [n_parts*splits][rows][heads][512] bf16 output.
+ * out          [n_parts*splits][rows][heads][512] output of out_dtype:
+ *              DSA_BF16 (the path's format, round to nearest even) or
+ *              DSA_FP32 (a checking mode: the same normalised values without
+ *              the bf16 rounding).
  * lse          [n_parts*splits][rows][heads] fp32 output.
  * Errors: INVALID_ARG (null pointers, heads not a positive multiple of 16,
  * splits outside [1, 64], rows*n_parts*splits*ceil(heads/128) above
- * 2^31 - 1, sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache not bf16/fp8).
+ * 2^31 - 1, sizes), UNSUPPORTED_K, UNSUPPORTED_DTYPE (cache not bf16/fp8,
+ * out_dtype not bf16/fp32).
  */
 int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads,
                           const void* cache, int32_t cache_dtype,
                           const float* cache_scale, int64_t num_slots,
                           const int32_t* slots, const int32_t* counts,
                           int32_t k, int32_t n_parts, int32_t splits,
-                          float sm_scale, void* out, float* lse,
-                          hipStream_t stream);
+                          float sm_scale, void* out, int32_t out_dtype,
+                          float* lse, hipStream_t stream);
 
 /*
  * dsa_lse_combine — LSE-weighted merge of per-shard partial attention.
@@ -227,15 +231,19 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads,
  *   lse = ln sum_p exp(lse_p) over finite lse_p (-inf if none)
  *   out = sum_p exp(lse_p - lse) * out_p       (0 if none)
  *
- * part_out  [n_parts][rows][heads][dim] bf16; part_lse [n_parts][rows][heads].
+ * part_out  [n_parts][rows][heads][dim] of part_dtype (DSA_BF16, or DSA_FP32
+ *           for the attention's fp32 checking mode); part_lse
+ *           [n_parts][rows][heads] fp32.
  * out       [rows][heads][dim] bf16 output; lse_out [rows][heads] fp32
  *           output (NULL: not written).
  * Errors: INVALID_ARG (null pointers, n_parts outside [1, 64], dim not a
- *         positive multiple of 8, sizes).
+ *         positive multiple of 8, sizes), UNSUPPORTED_DTYPE (part_dtype not
+ *         bf16/fp32).
  */
-int dsa_lse_combine(const void* part_out, const float* part_lse,
-                    int32_t n_parts, int32_t rows, int32_t heads, int32_t dim,
-                    void* out, float* lse_out, hipStream_t stream);
+int dsa_lse_combine(const void* part_out, int32_t part_dtype,
+                    const float* part_lse, int32_t n_parts, int32_t rows,
+                    int32_t heads, int32_t dim, void* out, float* lse_out,
+                    hipStream_t stream);
 
 /*
  * dsa_fused_rmsnorm_rope — RMSNorm over kv_c + interleaved-pair RoPE over

@@ -42,8 +42,8 @@ SIGNATURES = {
     "dsa_merge_convert": [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _I64, _I64, _I32, _I32,
                           _I32, _I32, _I32, _P, _P, _P],
     "dsa_sparse_mla_decode": [_P, _I32, _I32, _P, _I32, _P, _I64, _P, _P, _I32, _I32, _I32, _F32,
-                              _P, _P, _P],
-    "dsa_lse_combine": [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
+                              _P, _I32, _P, _P],
+    "dsa_lse_combine": [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P],
     "dsa_fused_rmsnorm_rope": [_P, _I64, _P, _I64, _I32, _P, _F32, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                _P, _I64, _P, _I64, _P, _F32, _P, _P, _P, _I64, _P],
     "dsa_cache_insert": [_P, _I64, _P, _I64, _I32, _P, _I32, _P, _P, _I64, _P],
@@ -110,6 +110,15 @@ def _bits16(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise RuntimeError(f"{name} must be bf16 (got {t.dtype})")
     return t
+
+
+def _partial_dtype(t: torch.Tensor, name: str) -> int:
+    """Partial outputs are bf16 (or its raw 16-bit bits) or fp32."""
+    _need(t, name)
+    if t.dtype == torch.float32:
+        return DSA_FP32
+    _bits16(t, name)
+    return DSA_BF16
 
 
 def _shape(t: torch.Tensor, name: str, shape):
@@ -331,11 +340,13 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
                       counts: Optional[torch.Tensor], *, sm_scale: float, splits: int = 1,
                       cache_scale: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      stream=None):
+                      out_dtype: torch.dtype = torch.bfloat16, stream=None):
     """q [rows][heads][576] bf16; cache [...][576] bf16 or uint8 (fp8 e4m3 codes);
     slots [n_parts][rows][k]; returns out [n_parts*splits][rows][heads][512]
-    bf16 and lse [n_parts*splits][rows][heads] fp32 (split-K partials of part p
-    are p*splits .. p*splits + splits - 1)."""
+    and lse [n_parts*splits][rows][heads] fp32 (split-K partials of part p
+    are p*splits .. p*splits + splits - 1).  out is bf16, or fp32 (the
+    checking mode without the bf16 rounding) when out_dtype is torch.float32
+    or a given `out` is fp32."""
     _bits16(q, "q")
     if q.dim() != 3 or q.shape[2] != 576:
         raise RuntimeError(f"q must be [rows][heads][576] (got {list(q.shape)})")
@@ -357,10 +368,12 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
         _contig(counts, "counts")
     P = n_parts * int(splits)
     if out is None:
-        out = torch.empty((P, rows, heads, 512), dtype=torch.bfloat16, device=q.device)
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise RuntimeError(f"out_dtype must be bf16 or fp32 (got {out_dtype})")
+        out = torch.empty((P, rows, heads, 512), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((P, rows, heads), dtype=torch.float32, device=q.device)
-    _bits16(out, "out")
+    odt = _partial_dtype(out, "out")
     _shape(out, "out", (P, rows, heads, 512))
     _contig(out, "out")
     _need(lse, "lse", torch.float32)
@@ -369,7 +382,7 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
     _same_device(q, cache, slots, counts, cache_scale, out, lse)
     _check(lib().dsa_sparse_mla_decode(
         _ptr(q), rows, heads, _ptr(cache), cdt, _ptr(cache_scale), num_slots, _ptr(slots),
-        _ptr(counts), k, n_parts, int(splits), float(sm_scale), _ptr(out), _ptr(lse),
+        _ptr(counts), k, n_parts, int(splits), float(sm_scale), _ptr(out), odt, _ptr(lse),
         _stream(stream)))
     return out, lse
 
@@ -377,8 +390,9 @@ def sparse_mla_decode(q: torch.Tensor, cache: torch.Tensor, slots: torch.Tensor,
 def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, *,
                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                 want_lse: bool = True, stream=None):
-    """part_out [n_parts][rows][heads][dim] bf16, part_lse [n_parts][rows][heads]."""
-    _bits16(part_out, "part_out")
+    """part_out [n_parts][rows][heads][dim] bf16 (or fp32, the attention's
+    checking mode), part_lse [n_parts][rows][heads]; out is bf16."""
+    pdt = _partial_dtype(part_out, "part_out")
     _need(part_lse, "part_lse", torch.float32)
     if part_out.dim() != 4:
         raise RuntimeError("part_out must be [n_parts][rows][heads][dim]")
@@ -398,7 +412,7 @@ def lse_combine(part_out: torch.Tensor, part_lse: torch.Tensor, *,
         _shape(lse_out, "lse_out", (rows, heads))
         _contig(lse_out, "lse_out")
     _same_device(part_out, part_lse, out, lse_out)
-    _check(lib().dsa_lse_combine(_ptr(part_out), _ptr(part_lse), n_parts, rows, heads, dim,
+    _check(lib().dsa_lse_combine(_ptr(part_out), pdt, _ptr(part_lse), n_parts, rows, heads, dim,
                                  _ptr(out), _ptr(lse_out), _stream(stream)))
     return out, lse_out
 

@@ -148,8 +148,11 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void
                           int32_t cache_dtype, const float* cache_scale, int64_t num_slots,
                           const int32_t* slots, const int32_t* counts, int32_t k,
                           int32_t n_parts, int32_t splits, float sm_scale, void* out,
-                          float* lse, hipStream_t stream) {
+                          int32_t out_dtype, float* lse, hipStream_t stream) {
   const char* fn = "dsa_sparse_mla_decode";
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32)
+    return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: output dtype %d is not bf16 or fp32", fn,
+                out_dtype);
   if (!q || !cache || !slots || !out || !lse)
     return fail(DSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "%s: rows=%d < 0", fn, rows);
@@ -177,14 +180,18 @@ int dsa_sparse_mla_decode(const void* q, int32_t rows, int32_t heads, const void
     return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer (q, cache, out need 16 bytes)", fn);
   if (rows == 0) return DSA_OK;
   dsa::launch_sparse_mla_decode(q, rows, heads, cache, cache_dtype == DSA_FP8_E4M3, cache_scale,
-                                num_slots, slots, counts, k, n_parts, splits, sm_scale, out, lse,
-                                stream);
+                                num_slots, slots, counts, k, n_parts, splits, sm_scale, out,
+                                out_dtype == DSA_FP32, lse, stream);
   return launched(fn);
 }
 
-int dsa_lse_combine(const void* part_out, const float* part_lse, int32_t n_parts, int32_t rows,
-                    int32_t heads, int32_t dim, void* out, float* lse_out, hipStream_t stream) {
+int dsa_lse_combine(const void* part_out, int32_t part_dtype, const float* part_lse,
+                    int32_t n_parts, int32_t rows, int32_t heads, int32_t dim, void* out,
+                    float* lse_out, hipStream_t stream) {
   const char* fn = "dsa_lse_combine";
+  if (part_dtype != DSA_BF16 && part_dtype != DSA_FP32)
+    return fail(DSA_ERR_UNSUPPORTED_DTYPE, "%s: partial dtype %d is not bf16 or fp32", fn,
+                part_dtype);
   if (!part_out || !part_lse || !out) return fail(DSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (n_parts < 1 || n_parts > 64)
     return fail(DSA_ERR_INVALID_ARG, "%s: n_parts=%d outside [1, 64]", fn, n_parts);
@@ -194,7 +201,8 @@ int dsa_lse_combine(const void* part_out, const float* part_lse, int32_t n_parts
   if (!aligned(part_out, 16) || !aligned(out, 16) || !aligned(part_lse, 4) || !aligned(lse_out, 4))
     return fail(DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (rows == 0 || heads == 0) return DSA_OK;
-  dsa::launch_lse_combine(part_out, part_lse, n_parts, rows, heads, dim, out, lse_out, stream);
+  dsa::launch_lse_combine(part_out, part_dtype == DSA_FP32, part_lse, n_parts, rows, heads, dim,
+                          out, lse_out, stream);
   return launched(fn);
 }
 

@@ -26,10 +26,10 @@ int launch_convert_index(const int* ids, int rows, int k, const int* row_req, in
 int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cache, bool fp8,
                              const float* cache_scale, int64_t num_slots, const int* slots,
                              const int* counts, int k, int n_parts, int splits, float sm_scale,
-                             void* out, float* lse, hipStream_t stream);
+                             void* out, bool f32out, float* lse, hipStream_t stream);
 
-int launch_lse_combine(const void* part_out, const float* part_lse, int P, int rows, int heads,
-                       int dim, void* out, float* lse_out, hipStream_t stream);
+int launch_lse_combine(const void* part_out, bool f32in, const float* part_lse, int P, int rows,
+                       int heads, int dim, void* out, float* lse_out, hipStream_t stream);
 
 int launch_cache_insert(const void* kv_c, int64_t kv_ld, const void* k_pe, int64_t pe_ld, int T,
                         void* cache, int cache_kind, const float* cache_scale,

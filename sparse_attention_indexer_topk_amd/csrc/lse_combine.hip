@@ -7,7 +7,9 @@
 // A (row, head) whose partials are all empty gets out = 0, lse = -inf.
 //
 // How: a pure streaming kernel — one thread per (row, head, 8 features),
-// fp32 accumulation in partial order, 16-byte bf16 store.  With at most 8
+// fp32 accumulation in partial order, 16-byte bf16 store.  The partials are
+// bf16 (the path's format) or fp32 (the attention's checking mode), read as
+// one 16-byte or two 16-byte slices per partial.  With at most 8
 // or 16 partials every load (the partial LSEs and the 16-byte output slices)
 // is issued before the first is used, so a thread makes one memory round
 // trip; more partials are taken four at a time.
@@ -27,6 +29,37 @@ __device__ __forceinline__ void accumulate8(float (&acc)[8], float w, const uint
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] += w * bf16_to_f32((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
 }
+// the same for 8 fp32 values
+__device__ __forceinline__ void accumulate8(float (&acc)[8], float w, const float4 a,
+                                            const float4 b) {
+  const bool on = w != 0.f;
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] += w * (on ? x[e] : 0.f);
+}
+// 8 partial values of one (row, head) as held in registers
+template <bool F32>
+struct Slice8;
+template <>
+struct Slice8<false> {
+  uint4 v;
+  __device__ __forceinline__ void zero() { v = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void add_to(float (&acc)[8], float w) const { accumulate8(acc, w, v); }
+};
+template <>
+struct Slice8<true> {
+  float4 a, b;
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void load(const void* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void add_to(float (&acc)[8], float w) const {
+    accumulate8(acc, w, a, b);
+  }
+};
+
 // fp32 pair -> packed bf16 (lo in the low half), hardware round to nearest even
 __device__ __forceinline__ uint32_t cvt_pk_bf16c(float lo, float hi) {
   typedef __bf16 bf16x2c_t __attribute__((ext_vector_type(2)));
@@ -34,32 +67,35 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16c(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// NF > 0: up to NF partials, all loads in flight at once; NF == 0: any number
-template <int NF>
+// NF > 0: up to NF partials, all loads in flight at once; NF == 0: any number.
+// F32: fp32 partials.
+template <int NF, bool F32>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
-    const uint16_t* __restrict__ pout, const float* __restrict__ plse, int P, int64_t rh_total,
+    const void* __restrict__ pout, const float* __restrict__ plse, int P, int64_t rh_total,
     int dim, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   const int chunks = dim / 8;
   const int64_t gid = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
   if (gid >= rh_total * chunks) return;
   const int64_t rh = gid / chunks;
   const int c = (int)(gid % chunks);
+  constexpr int kElem = F32 ? 4 : 2;   // bytes per partial value
   auto slice = [&](int p) {
-    return reinterpret_cast<const uint4*>(pout + ((int64_t)p * rh_total + rh) * dim + c * 8);
+    return reinterpret_cast<const uint8_t*>(pout) +
+           (((int64_t)p * rh_total + rh) * dim + c * 8) * kElem;
   };
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f, M = -INFINITY;
   if constexpr (NF > 0) {
     float l[NF];
-    uint4 v[NF];
+    Slice8<F32> v[NF];
 #pragma unroll
     for (int p = 0; p < NF; ++p) {
       l[p] = -INFINITY;
-      v[p] = make_uint4(0u, 0u, 0u, 0u);
+      v[p].zero();
       if (p < P) {
         l[p] = plse[(int64_t)p * rh_total + rh];
-        v[p] = *slice(p);
+        v[p].load(slice(p));
       }
     }
 #pragma unroll
@@ -69,7 +105,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
       for (int p = 0; p < NF; ++p) {
         const float w = exp2f((l[p] - M) * kLog2eC);   // exp(-inf) = 0
         z += w;
-        accumulate8(acc, w, v[p]);
+        v[p].add_to(acc, w);
       }
     }
   } else {
@@ -77,22 +113,22 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
     if (M != -INFINITY) {
       constexpr int B = 4;
       for (int p0 = 0; p0 < P; p0 += B) {
-        uint4 v[B];
+        Slice8<F32> v[B];
         float w[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const int p = p0 + b;
           w[b] = 0.f;
-          v[b] = make_uint4(0u, 0u, 0u, 0u);
+          v[b].zero();
           if (p < P) {
             w[b] = exp2f((plse[(int64_t)p * rh_total + rh] - M) * kLog2eC);
-            v[b] = *slice(p);
+            v[b].load(slice(p));
           }
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           z += w[b];
-          accumulate8(acc, w[b], v[b]);
+          v[b].add_to(acc, w[b]);
         }
       }
     }
@@ -106,22 +142,25 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
   if (lse_out && c == 0) lse_out[rh] = (M == -INFINITY) ? -INFINITY : M + logf(z);
 }
 
-int launch_lse_combine(const void* part_out, const float* part_lse, int P, int rows, int heads,
-                       int dim, void* out, float* lse_out, hipStream_t stream) {
+int launch_lse_combine(const void* part_out, bool f32in, const float* part_lse, int P, int rows,
+                       int heads, int dim, void* out, float* lse_out, hipStream_t stream) {
   const int64_t rh = (int64_t)rows * heads;
   const int64_t threads = rh * (dim / 8);
   const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
-  const uint16_t* po = reinterpret_cast<const uint16_t*>(part_out);
   uint16_t* o = reinterpret_cast<uint16_t*>(out);
-  if (P <= 8)
-    hipLaunchKernelGGL(lse_combine_kernel<8>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
-                       stream, po, part_lse, P, rh, dim, o, lse_out);
-  else if (P <= kCombineFast)
-    hipLaunchKernelGGL(lse_combine_kernel<kCombineFast>, dim3((unsigned)blocks),
-                       dim3(kCombineThreads), 0, stream, po, part_lse, P, rh, dim, o, lse_out);
-  else
-    hipLaunchKernelGGL(lse_combine_kernel<0>, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
-                       stream, po, part_lse, P, rh, dim, o, lse_out);
+#define DSA_COMBINE(NF, F32)                                                                 \
+  hipLaunchKernelGGL((lse_combine_kernel<NF, F32>), dim3((unsigned)blocks),                  \
+                     dim3(kCombineThreads), 0, stream, part_out, part_lse, P, rh, dim, o, lse_out)
+  if (f32in) {
+    if (P <= 8) DSA_COMBINE(8, true);
+    else if (P <= kCombineFast) DSA_COMBINE(kCombineFast, true);
+    else DSA_COMBINE(0, true);
+  } else {
+    if (P <= 8) DSA_COMBINE(8, false);
+    else if (P <= kCombineFast) DSA_COMBINE(kCombineFast, false);
+    else DSA_COMBINE(0, false);
+  }
+#undef DSA_COMBINE
   return 0;
 }
 

@@ -232,12 +232,15 @@ __device__ __forceinline__ int lane_now() {
   return l;
 }
 
-template <bool FP8, bool OFF32, bool FULL>
+// F32OUT: the partial outputs are written as fp32 (a checking mode: no
+// bf16 rounding between the attention and the combine), straight from the
+// accumulators, 16 bytes (4 features of one head) per lane and store
+template <bool FP8, bool OFF32, bool FULL, bool F32OUT>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q, int rows, int heads, const uint8_t* __restrict__ cache,
     const float* __restrict__ cache_scale, int64_t num_slots, const int* __restrict__ slots,
     const int* __restrict__ counts, int k, int splits, float sm_scale,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    void* __restrict__ out_v, float* __restrict__ lse) {
   using Lay = AttnLayout<FP8>;
   constexpr int kDmaMax = Lay::kDmaMax;
   __shared__ __attribute__((aligned(16))) uint8_t s_tiles[Lay::kTilesB];
@@ -650,6 +653,26 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   }
   lgkm_wait0();
   bar();   // 1/l of every head published; every wave done with the ring
+  if constexpr (F32OUT) {
+    // lane (n16, g4) holds features 64*wave + 16*f + 4*g4 .. +4 of head
+    // 16*hb + n16 in o[f][hb]
+    float* ob = reinterpret_cast<float*>(out_v) +
+                (((int64_t)out_part * rows + row) * heads + hg * kHPB) * kValue;
+#pragma unroll
+    for (int hb = 0; hb < kNHB; ++hb) {
+      if (hb < n_hb) {
+        const float inv = s_inv[16 * hb + e_n16];
+        float* orow = ob + (int64_t)(16 * hb + e_n16) * kValue + 64 * wave + 4 * e_g4;
+#pragma unroll
+        for (int f = 0; f < kFBW; ++f)
+          *reinterpret_cast<float4*>(orow + 16 * f) =
+              make_float4(o[f][hb][0] * inv, o[f][hb][1] * inv, o[f][hb][2] * inv,
+                          o[f][hb][3] * inv);
+      }
+    }
+    return;
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(out_v);
   // staging: head rows of 512 bf16 outputs, padded by 16 bytes so that the
   // row-strided 8-byte writes spread over the banks
 #pragma unroll
@@ -680,23 +703,27 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 int launch_sparse_mla_decode(const void* q, int rows, int heads, const void* cache, bool fp8,
                              const float* cache_scale, int64_t num_slots, const int* slots,
                              const int* counts, int k, int n_parts, int splits, float sm_scale,
-                             void* out, float* lse, hipStream_t stream) {
+                             void* out, bool f32out, float* lse, hipStream_t stream) {
   dim3 grid(rows, n_parts * splits, (heads + kHPB - 1) / kHPB);
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cache);
-  uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
   // 32-bit gather offsets when the whole pool lies within 4 GiB of its base
   const bool off32 = num_slots * (int64_t)(fp8 ? kRowB8 : kRowB) <= (int64_t)0xffffffffLL;
   const bool full = heads % kHPB == 0;
+  // fp32 partials (the checking mode) take the general head-group variant
 #define DSA_ATTN(F, O)                                                                       \
-  if (full)                                                                                  \
-    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, true>), grid, dim3(kAttnThreads), 0,   \
-                       stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, \
-                       splits, sm_scale, o16, lse);                                           \
+  if (f32out)                                                                                \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, false, true>), grid, dim3(kAttnThreads), \
+                       0, stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, \
+                       k, splits, sm_scale, out, lse);                                        \
+  else if (full)                                                                             \
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, true, false>), grid, dim3(kAttnThreads), \
+                       0, stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, \
+                       k, splits, sm_scale, out, lse);                                        \
   else                                                                                       \
-    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, false>), grid, dim3(kAttnThreads), 0,  \
-                       stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, k, \
-                       splits, sm_scale, o16, lse)
+    hipLaunchKernelGGL((sparse_mla_decode_kernel<F, O, false, false>), grid, dim3(kAttnThreads), \
+                       0, stream, q16, rows, heads, c8, cache_scale, num_slots, slots, counts, \
+                       k, splits, sm_scale, out, lse)
   if (fp8) {
     if (off32) { DSA_ATTN(true, true); }
     else { DSA_ATTN(true, false); }

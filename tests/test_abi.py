@@ -103,11 +103,12 @@ def test_sparse_mla_decode_rejects():
     f = L.dsa_sparse_mla_decode
     def call(**kw):
         a = dict(q=FAKE, rows=0, heads=128, cache=FAKE, dt=dsa.DSA_BF16, scale=None, nslots=100,
-                 slots=FAKE, counts=None, k=2048, parts=4, splits=1, sm=0.04, out=FAKE, lse=FAKE)
+                 slots=FAKE, counts=None, k=2048, parts=4, splits=1, sm=0.04, out=FAKE,
+                 odt=dsa.DSA_BF16, lse=FAKE)
         a.update(kw)
         return f(a["q"], a["rows"], a["heads"], a["cache"], a["dt"], a["scale"], a["nslots"],
                  a["slots"], a["counts"], a["k"], a["parts"], a["splits"], a["sm"], a["out"],
-                 a["lse"], None)
+                 a["odt"], a["lse"], None)
     assert call() == OK
     assert call(heads=24) == INV
     assert call(heads=0) == INV
@@ -124,15 +125,22 @@ def test_sparse_mla_decode_rejects():
     # workgroup count past 2^31 - 1 is refused before any launch
     assert call(rows=1 << 29, parts=4, heads=128) == INV
     assert call(rows=1 << 28, parts=4, splits=2, heads=128) == INV
+    # partial outputs: bf16, or fp32 (the checking mode); nothing else
+    assert call(odt=dsa.DSA_FP32) == OK
+    assert call(odt=dsa.DSA_FP8_E4M3) == BADT
+    assert call(odt=0) == BADT
 
 
 def test_lse_combine_rejects():
     f = L.dsa_lse_combine
-    assert f(FAKE, FAKE, 4, 0, 128, 512, FAKE, None, None) == OK
-    assert f(FAKE, FAKE, 0, 0, 128, 512, FAKE, None, None) == INV
-    assert f(FAKE, FAKE, 65, 0, 128, 512, FAKE, None, None) == INV
-    assert f(FAKE, FAKE, 4, 0, 128, 12, FAKE, None, None) == INV
-    assert f(None, FAKE, 4, 0, 128, 512, FAKE, None, None) == INV
+    B, F = dsa.DSA_BF16, dsa.DSA_FP32
+    assert f(FAKE, B, FAKE, 4, 0, 128, 512, FAKE, None, None) == OK
+    assert f(FAKE, F, FAKE, 4, 0, 128, 512, FAKE, None, None) == OK
+    assert f(FAKE, dsa.DSA_FP8_E4M3, FAKE, 4, 0, 128, 512, FAKE, None, None) == BADT
+    assert f(FAKE, B, FAKE, 0, 0, 128, 512, FAKE, None, None) == INV
+    assert f(FAKE, B, FAKE, 65, 0, 128, 512, FAKE, None, None) == INV
+    assert f(FAKE, B, FAKE, 4, 0, 128, 12, FAKE, None, None) == INV
+    assert f(None, B, FAKE, 4, 0, 128, 512, FAKE, None, None) == INV
 
 
 def test_fused_rmsnorm_rope_rejects():
