@@ -5,7 +5,8 @@
 * the five full-size workloads in the launch configuration the benchmark
   times: every row of the decode, long and fp8 workloads at every stage, and
   256 (integer stages) and 18 (attention) rows spread over the prefill chunk;
-* determinism: two runs are bit-identical.
+* determinism: two runs are bit-identical;
+* 20 seeded random shapes through every stage.
 """
 import sys
 
@@ -85,7 +86,45 @@ def host_cache_after_insert(c, rows_oracle):
 @pytest.mark.parametrize("name", list(dsa_inputs.PARITY_CASES))
 def test_path_matches_oracle_every_stage(name):
     log(f"[parity] case {name}")
-    c = dsa_inputs.make(name)
+    check_every_stage(dsa_inputs.make(name))
+
+
+def random_spec(i):
+    """A seeded random shape: 1-16 shards with assorted interleaves, k of 512,
+    1024 or 2048, shard rows from a few hundred positions to chunked sweeps,
+    16-144 heads, bf16 or fp8 caches, window and mixed row bounds, a shared
+    request or multi-token rows, sometimes the fused prologue."""
+    r = np.random.default_rng(7000 + i)
+    S = int(r.choice([1, 2, 3, 4, 5, 8, 16]))
+    I = int(r.choice([1, 2, 3, 7, 64]))
+    k = int(r.choice([512, 1024, 2048]))
+    q_len = int(r.choice([1, 1, 2]))
+    rows = q_len * int(r.integers(1, 4))
+    # per-shard length first: short rows, one resident chunk, chunked sweeps
+    local = int(r.choice([int(r.integers(600, 3000)), int(r.integers(3000, 12000)),
+                          int(r.integers(12000, 40000))]))
+    ctx = max(1200, min(local * S, 64000))
+    cache = str(r.choice(["bf16", "fp8"]))
+    return dsa_inputs.Spec(
+        f"rand{i}", rows=rows, ctx=ctx, shards=S, interleave=I, k=k,
+        heads=int(r.choice([16, 32, 48, 64, 128, 144])), seed=9000 + i,
+        logits=str(r.choice(["normal", "rounded64", "bumps"])), cache=cache,
+        latent_std=float(r.choice([1.0, 1.0 / 24.0])),
+        one_request=bool(q_len == 1 and r.random() < 0.25),
+        row_ends=None if q_len > 1 else r.choice([None, "mixed"]),
+        row_starts=r.choice([None, "window"]),
+        prologue=bool(r.random() < 0.3), q_len=q_len)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_shapes_every_stage(i):
+    sp = random_spec(i)
+    log(f"[parity] random case {i}: {sp}")
+    check_every_stage(dsa_inputs.make(sp))
+
+
+def check_every_stage(c):
+    """Every stage of one case, element by element against the oracle."""
     path = DecodePath(**dsa_inputs.device_arrays(c))
     cache_ref = c.cache
     if c.spec.prologue:
