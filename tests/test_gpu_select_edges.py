@@ -21,8 +21,8 @@ output.
 Every selection result is compared element by element (bit for bit) with the
 oracle.
 
-Attention: a bf16 pool larger than 4 GiB (the 64-bit gather addresses),
-against the oracle to the attention tolerance.
+Attention: bf16 and fp8 pools larger than 4 GiB (the 64-bit gather
+addresses), against the oracle to the attention tolerance.
 """
 import sys
 
@@ -30,6 +30,7 @@ import numpy as np
 import pytest
 import torch
 
+import dsa_inputs
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -355,3 +356,48 @@ def test_attention_pool_beyond_4gib_bf16():
     torch.cuda.empty_cache()
     bad = attn_mismatch(bf16_bits_to_f64(got), po, lse.cpu().numpy(), pl)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_attention_pool_beyond_4gib_fp8(splits):
+    """An fp8 pool larger than 4 GiB (576-byte rows) gathers with 64-bit
+    addresses too; rows near its end and near its start, split-K or not."""
+    from dsa_testlib import attn_mismatch, bf16_bits_to_f64
+    n_slots = (1 << 32) // 576 + 40_000             # just past 4 GiB of fp8 rows
+    R, H, k = 2, 32, 512
+    r = np.random.default_rng(22 + splits)
+    counts = np.array([[k, 300]], np.int32)
+    slots = np.full((1, R, k), -1, np.int32)
+    for i in range(R):
+        c = counts[0, i]
+        hi = r.choice(np.arange(n_slots - 60_000, n_slots), size=c // 2, replace=False)
+        lo = r.choice(60_000, size=c - c // 2, replace=False)
+        slots[0, i, :c] = np.concatenate([hi, lo])
+    used = np.unique(slots[slots >= 0])
+    scale = np.float32(2.0 ** -4)
+    # rows as the workloads draw them: N(0, 1) / scale rounded to e4m3
+    codes = dsa_inputs._draw_fp8_normal(r, (len(used), 576), 1.0 / float(scale))
+    q = (r.standard_normal((R, H, 576)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    log(f"attention fp8 pool {n_slots} slots ({n_slots * 576 / 2**30:.2f} GiB), splits {splits}")
+    cache = torch.empty((n_slots, 576), dtype=torch.uint8, device=DEV)
+    cache[torch.from_numpy(used.astype(np.int64)).to(DEV)] = torch.from_numpy(codes).to(DEV)
+    sm_scale = float(np.float32(1.0 / 24.0))
+    out, lse = dsa.sparse_mla_decode(torch.from_numpy(q.view(np.int16)).to(DEV).view(torch.bfloat16),
+                                     cache, torch.from_numpy(slots).to(DEV),
+                                     torch.from_numpy(counts).to(DEV), sm_scale=sm_scale,
+                                     splits=splits,
+                                     cache_scale=torch.tensor([scale], device=DEV))
+    torch.cuda.synchronize()
+    remap = {int(s): j for j, s in enumerate(used)}
+    oslots = np.vectorize(lambda s: remap.get(int(s), -1))(slots).astype(np.int32)
+    po, pl = oracle.sparse_mla_partial(q, codes, "fp8", scale, oslots, counts, sm_scale)
+    got = bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    gl = lse.cpu().numpy().astype(np.float64)
+    del cache
+    torch.cuda.empty_cache()
+    if splits > 1:   # merge the split-K partials with the oracle's combine
+        got, gl = oracle.lse_combine(got, gl)
+        got, gl = got[None], gl[None]
+    bad = attn_mismatch(got, po, gl, pl)
+    assert not bad, bad
+
