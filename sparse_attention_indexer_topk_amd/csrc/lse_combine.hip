@@ -6,11 +6,13 @@
 //   lse = ln sum_p exp(lse_p) over finite lse_p, out = sum_p exp(lse_p - lse) out_p.
 // A (row, head) whose partials are all empty gets out = 0, lse = -inf.
 //
-// How: a pure streaming kernel — one thread per (row, head) and two 8-feature
-// slices half a row apart (one slice when the row holds an odd number of
-// them), fp32 accumulation in partial order, 16-byte bf16 stores.  Two
-// slices per thread keep twice the bytes in flight per wave: decode 7.6
-// against 8.6 us.  The partials are
+// How: a pure streaming kernel — one thread per (row, head) and one 8-feature
+// slice, or two slices half a row apart for small launches, fp32
+// accumulation in partial order, 16-byte bf16 stores.  Two slices per thread
+// keep twice the bytes in flight per wave where the launch is too small to
+// fill the memory system with threads (at most 8 partials and 64K (row,
+// head) pairs: decode 8.6 -> 7.8 us, fp8 15.5 -> 14.4 us); with more
+// partials, or a launch as large as a prefill chunk, they were slower.  The partials are
 // bf16 (the path's format) or fp32 (the attention's checking mode), read as
 // one 16-byte or two 16-byte slices per partial.  With at most 8
 // or 16 partials every load (the partial LSEs and the 16-byte output slices)
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(
 int launch_lse_combine(const void* part_out, bool f32in, const float* part_lse, int P, int rows,
                        int heads, int dim, void* out, float* lse_out, hipStream_t stream) {
   const int64_t rh = (int64_t)rows * heads;
-  const int nc = (dim / 8) % 2 == 0 ? 2 : 1;
+  const int nc = ((dim / 8) % 2 == 0 && P <= 8 && rh <= 65536) ? 2 : 1;
   const int64_t threads = rh * (dim / 8 / nc);
   const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads;
   uint16_t* o = reinterpret_cast<uint16_t*>(out);
