@@ -146,6 +146,10 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(uint32_t addr) {
 }
 // wait until at most N LDS operations of this wave are in flight
 template <int N>
+__device__ __forceinline__ void lgkm_wait_1(u32x4_t& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
 __device__ __forceinline__ void lgkm_wait_2(u32x4_t& a, u32x4_t& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
@@ -467,10 +471,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     }
   };
   // O^T += V^T P^T for this wave's 4 feature blocks and every present head
-  // block; the P^T of head block hb is what lane `lane` of score wave hb wrote
+  // block; the P^T of head block hb is what lane `lane` of score wave hb wrote.
+  // bf16: the P^T fragments go through a ring of two, read one head block
+  // ahead of its products, the first two requested with the value fragments
+  // (read as they are used, each read's round trip stalls the wave before
+  // its 4 products: decode 62.7 -> 58.8 us).  fp8 keeps the plain reads: with
+  // its conversions the ring's 4 registers cost more than the overlap gains.
   auto values = [&](int tt) {
-    const uint8_t* pb = s_p[tt & 1] + 16 * lane;
     bf16x8_t va[kFBW];
+    u32x4_t pr[2];
+    uint32_t pb = 0;
+    if constexpr (!FP8) pb = (uint32_t)(uintptr_t)(lds_void_ptr)(s_p[tt & 1] + 16 * lane_now());
     if constexpr (FP8) {
       // features 16*(4*wave + f) + lane%16, 8 tokens in the P^T order
       const uint32_t vb =
@@ -494,23 +505,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         r[2 * f] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1)>(vb);
         r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1) + 1024>(vb);
       });
-      lgkm_wait_4v<0>(r[0], r[1], r[2], r[3]);
-      lgkm_wait_4v<0>(r[4], r[5], r[6], r[7]);
+      pr[0] = lds_read_b128<0>(pb);
+      pr[1] = lds_read_b128<1024>(pb);
+      lgkm_wait_4v<2>(r[0], r[1], r[2], r[3]);
+      lgkm_wait_4v<2>(r[4], r[5], r[6], r[7]);
 #pragma unroll
       for (int f = 0; f < kFBW; ++f)
         va[f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2, 3));
     }
-    bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pb);
+    if constexpr (FP8) {
+      const uint8_t* pp = s_p[tt & 1] + 16 * lane;
+      bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pp);
 #pragma unroll
-    for (int hb = 0; hb < kNHB; ++hb) {
-      if (hb < n_hb) {
-        bf16x8_t pn = pa;
-        if (hb + 1 < n_hb) pn = *reinterpret_cast<const bf16x8_t*>(pb + 1024 * (hb + 1));
+      for (int hb = 0; hb < kNHB; ++hb) {
+        if (hb < n_hb) {
+          bf16x8_t pn = pa;
+          if (hb + 1 < n_hb) pn = *reinterpret_cast<const bf16x8_t*>(pp + 1024 * (hb + 1));
 #pragma unroll
-        for (int f = 0; f < kFBW; ++f)
-          o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
-        pa = pn;
+          for (int f = 0; f < kFBW; ++f)
+            o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
+          pa = pn;
+        }
       }
+    } else {
+      // every head block's fragment is read (s_p holds all 8; absent blocks
+      // are never used), so the ring's wait counts are fixed
+      static_for<kNHB>([&](auto hc) {
+        constexpr int hb = decltype(hc)::value;
+        lgkm_wait_1<hb + 1 < kNHB ? 1 : 0>(pr[hb & 1]);
+        if (hb < n_hb) {
+          const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pr[hb & 1]);
+#pragma unroll
+          for (int f = 0; f < kFBW; ++f)
+            o[f][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[f], pa, o[f][hb], 0, 0, 0);
+        }
+        if constexpr (hb + 2 < kNHB) pr[hb & 1] = lds_read_b128<1024 * (hb + 2)>(pb);
+      });
     }
   };
   // mask, softmax against the reference max, P^T of tile tt to LDS.  sv: the
