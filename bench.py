@@ -52,6 +52,9 @@ def parse():
                    help="merge_candidates and convert_index as two launches")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="oracle time per CPU-baseline mode (single thread, all threads)")
+    p.add_argument("--splits", type=int, default=None,
+                   help="pieces each shard's token list is cut into for the attention "
+                        "(default: enough workgroups to cover the CUs)")
     p.add_argument("--launch-floor", action="store_true",
                    help="only launch empty kernels with the grid shapes of the decode step's "
                         "kernels (30 each), for a kernel trace of the launch floor")
@@ -226,6 +229,8 @@ def main():
             print("--pcp needs a workload with a prologue (fp8)", file=sys.stderr)
             sys.exit(2)
         arrays["pcp_ranks"] = a.pcp
+    if a.splits is not None:
+        arrays["splits"] = a.splits
     path = DecodePath(**arrays)
     path.want_ids = a.unfused or not a.no_merge_ids
     logits_sets, q_sets = [path.logits], [path.q]
@@ -349,6 +354,7 @@ def main():
         "config": {"workload": c.spec.name, "rows": c.rows, "ctx": c.ctx, "k": c.k,
                    "shards": c.S, "interleave": c.I, "heads": c.heads, "cache": c.cache_dtype,
                    "input_sets": a.sets, "merged_ids_written": bool(path.want_ids),
+                   "attention_splits": path.splits,
                    **({"pcp_ranks": a.pcp} if a.pcp else {})},
         "topk_rows_per_s": round(c.rows / t_topk, 1),
         "decode_tokens_per_s": round(c.rows / t_dec, 1),
