@@ -22,11 +22,13 @@
 //    HBM into LDS with global_load_lds_dwordx4 (no register staging; a
 //    uniform base plus a 32-bit offset per lane when the pool spans less
 //    than 4 GiB); one barrier per tile;
-//  - the gather lays a tile out in LDS as blocks of 16 tokens x 16-byte
-//    chunks (1 KB): a score k-step reads one contiguous block and a value
-//    transpose read contiguous bytes, free of the bank conflicts that
-//    strided row reads meet on this LDS; one gather instruction fills one
-//    block;
+//  - the gather lays a tile out in LDS as blocks of 16 tokens x 4 16-byte
+//    chunks (1 KB), one gather instruction per block: each token's 64
+//    contiguous bytes go to 4 consecutive lanes, which the memory path takes
+//    as one request (a token per lane, the same bytes gathered 10 % slower),
+//    and the 4 chunks of a token are permuted by its position so that the
+//    score reads (16 tokens, one chunk) and the value transpose reads meet
+//    no LDS bank conflict;
 //  - scores are computed transposed, S^T = K Q^T (rows = tokens), so each
 //    lane ends with 8 tokens of ONE head — with the token order inside the
 //    k dimension permuted the same way on both operands, exactly the B
@@ -334,32 +336,49 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   lgkm_wait0();
   bar();   // first slot entries and flags ready
 
-  // ---- lane-invariant LDS byte offsets ----------------------------------------
-  // bf16 tile: block (c/4)*2 + t/16 holds tokens 16*(t/16) .. +16 x 16-byte
-  // chunks 4*(c/4) .. +4 (32 features), token t, chunk c in slot (t % 16) +
-  // 16 * (c % 4).  A score k-step kk reads blocks 2kk and 2kk+1 at lane * 16.
-  // Value transpose reads: in 16-lane group g4, source lane s = n16 reads
-  // token 16*rd + 4*g4 + s/4 at features 16*fb + 4*(s%4): logical chunk 2fb +
-  // (s%4)/2, half s%2, at pv_base + 2048*(fb/2) + 512*(fb%2) + 1024*rd.
-  const int pv_base = ((4 * g4 + (n16 >> 2) + 16 * ((n16 & 3) >> 1)) << 4) + 8 * (n16 & 1);
-  // raw fp8 tile: the same block structure with 16-code chunks (64 features
-  // per block), token t in slot ((t % 16) ^ (8 * (t/16))) + 16 * (c % 4) (the
-  // xor keeps the two token halves that one transpose read touches on
-  // different banks).
-  //  - scores, k-step kk (chunks 2kk, 2kk+1), token block b: lane (n16, g4)
-  //    reads the 8 codes of features 32kk + 8*g4 .. +8 of token 16b + n16 at
-  //    qk8_base[b] + 2048*(kk/2) + 512*(kk%2);
-  //  - values, block fb (chunk fb): ds_read_b64_tr_b8 hands lane i of a
+  // ---- LDS tile layout and lane-invariant byte offsets ------------------------
+  // A tile is blocks of 1 KB: block 2x + h holds tokens 16h .. 16h+15 (t =
+  // token % 16) x chunks 4x .. 4x+3 (16 bytes each: 8 bf16 features, or 16
+  // fp8 codes).  Token t occupies slots 4t .. 4t+3, chunk 4x + c in slot 4t +
+  // (c ^ rot) with rot = 2*(t/8) (bf16) or 2*(t/8) ^ h (fp8).  The chunk's
+  // position is bits 4-5 of its byte offset, so another chunk of the same
+  // token is an xor of the offset away.  This LDS serves a 16-byte read in
+  // four passes over 16 lanes (lane bit 5 and the parity of lane bits 2-4
+  // select the pass), each pass needing 16 different 16-byte bank windows
+  // (address mod 256); in-bounds probes of every read pattern below time
+  // them at or under the cost of contiguous reads, where other rotations
+  // (by t/4, or none) doubled the score reads' cost.
+  //  - bf16 scores, k-step kk, token half b: lane (n16, g4) reads chunk g4 of
+  //    block 2kk + b for token n16 at qk_off + 2048*kk + 1024*b;
+  //  - bf16 values: in 16-lane group g4, source lane s = n16 reads token
+  //    16*rd + 4*g4 + s/4 at features 16*fb + 4*(s%4): chunk 2fb + (s%4)/2,
+  //    half s%2, at (pv_off ^ 32*(fb%2)) + 2048*(fb/2) + 1024*rd;
+  //  - fp8 scores, k-step kk, token half b: lane (n16, g4) reads the 8 codes
+  //    of features 32kk + 8*g4 .. +8 of token 16b + n16 (chunk 2kk + g4/2,
+  //    half g4%2) at (qo8_h ^ 32*(kk%2) ^ 16*b) + 2048*(kk/2) + 1024*b;
+  //  - fp8 values, block fb (chunk fb): ds_read_b64_tr_b8 hands lane i of a
   //    16-lane group byte i%8 of the 8-byte chunk addressed by lane 2e + i/8
   //    of its group as element e, so lane (s, g4) addresses half s%2 of the
   //    token that element s/2 stands for (4*g4 + e%4, + 16 for e >= 4), at
-  //    pv8_base + 2048*(fb/4) + 256*(fb%4); lane i then holds feature i of
+  //    (po8_h ^ 16*(fb%4)) + 2048*(fb/4); lane i then holds feature i of
   //    the block for the 8 tokens in the order of the P^T operand.
-  const int qk8_base0 = 16 * n16 + 256 * (g4 >> 1) + 8 * (g4 & 1);
-  const int qk8_base1 = 1024 + 16 * (n16 ^ 8) + 256 * (g4 >> 1) + 8 * (g4 & 1);
-  const int pv8_e = n16 >> 1;
-  const int pv8_base = 1024 * (pv8_e >> 2) + 16 * ((4 * g4 + (pv8_e & 3)) ^ (8 * (pv8_e >> 2))) +
-                       8 * (n16 & 1);
+  // The bf16 offsets are rebuilt from the lane index where they are used:
+  // held across the tile loop they would cost spill slots.
+  auto qk_off = [&]() {
+    const int l = lane_now(), m = l & 15, g = l >> 4;
+    return 16 * (4 * m + (g ^ (2 * (m >> 3))));
+  };
+  auto pv_off = [&]() {   // feature blocks of even fb; odd: xor 32
+    const int l = lane_now(), m = l & 15, g = l >> 4;
+    return 64 * (4 * g + (m >> 2)) + 32 * (g >> 1) + 16 * ((m >> 1) & 1) + 8 * (m & 1);
+  };
+  // fp8: the two offsets are held across the loop (registers are free there,
+  // and the conversions leave the wave less VALU time to rebuild them)
+  // scores: token half 0, even kk
+  const int qo8_h = FP8 ? 64 * n16 + 16 * ((g4 >> 1) ^ (2 * (n16 >> 3))) + 8 * (g4 & 1) : 0;
+  // values: chunk 4x of the block; chunk 4x + f: xor 16f
+  const int po8_h = FP8 ? 1024 * ((n16 >> 1) >> 2) + 64 * (4 * g4 + ((n16 >> 1) & 3)) +
+                              16 * ((2 * (g4 >> 1)) ^ ((n16 >> 1) >> 2)) + 8 * (n16 & 1) : 0;
 
   auto main_stage = [&](int tt) { return s_tiles + (tt % Lay::kMainStages) * Lay::kMainB; };
   auto rope_stage = [&](int tt) {
@@ -371,20 +390,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
   auto refills = [&](int u) {
     return wave == kRefillWave && u + Lay::kRefill >= kSlotInit && u + Lay::kRefill < ntiles;
   };
-  // gather instruction ins fills block ins: tokens 16*(ins%2) + lane%16
-  // (fp8: xor 8 on the second half), 16-byte chunks 4*(ins/2) + lane/16
-  auto tile_slots = [&](int u, int (&sv)[kDmaMax]) {
-#pragma unroll
-    for (int jj = 0; jj < kDmaMax; ++jj) {
-      const int ins = jj * kAttnWaves + wave;
-      sv[jj] = 0;
-      if (ins < Lay::kBlocks) {
-        const int t = 16 * (ins & 1) + ((lane & 15) ^ (FP8 ? 8 * (ins & 1) : 0));
-        sv[jj] = s_sring[(u % kSlotRing) * kTile + t];
-      }
-    }
+  // gather instruction ins fills block ins: lane l takes token 16*(ins%2) +
+  // l/4 and chunk 4*(ins/2) + ((l%4) ^ rot); a wave's instructions are ins =
+  // wave + 8j, so all of them cover the same 16 tokens and one slot entry per
+  // lane serves the wave's whole tile
+  auto tile_slot = [&](int u) {
+    return s_sring[(u % kSlotRing) * kTile + 16 * (wave & 1) + (lane_now() >> 2)];
   };
-  auto issue = [&](int u, const int (&sv)[kDmaMax]) {
+  auto issue = [&](int u, int sv) {
+    const int gl = lane_now();
+    const int g_rot = (2 * (gl >> 5)) ^ (FP8 ? (wave & 1) : 0);
     if (refills(u) && lane < kTile) {
       const int v = u + Lay::kRefill;
       const int i = t_lo + v * kTile + lane_now();
@@ -397,8 +412,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     for (int jj = 0; jj < kDmaMax; ++jj) {
       const int ins = jj * kAttnWaves + wave;
       if (ins < Lay::kBlocks) {
-        const int off = (4 * (ins >> 1) + (lane >> 4)) * 16;
-        const int s = (unsigned)sv[jj] < (unsigned)slot_lim ? sv[jj] : 0;
+        const int off = (4 * (ins >> 1) + ((gl & 3) ^ g_rot)) * 16;
+        const int s = (unsigned)sv < (unsigned)slot_lim ? sv : 0;
         const uint8_t* src;
         if constexpr (OFF32)
           src = cache + (uint32_t)((uint32_t)s * (uint32_t)Lay::kRowBytes + (uint32_t)off);
@@ -419,19 +434,21 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     if (!wave_on) return;
     constexpr int A = Lay::kKAhead;
     if constexpr (FP8) {
-      const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + qk8_base0);
-      const uint32_t m1 = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + qk8_base1);
-      const uint32_t r0 = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + qk8_base0);
-      const uint32_t r1 = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + qk8_base1);
+      // key offsets: half 0 even kk qo, odd qo ^ 32; half 1 even qo ^ 16,
+      // odd qo ^ 48 (plus 1024)
+      const int qo = qo8_h;
+      const uint32_t ms = (uint32_t)(uintptr_t)(lds_void_ptr)main_stage(tt);
+      const uint32_t rs = (uint32_t)(uintptr_t)(lds_void_ptr)rope_stage(tt);
+      const uint32_t m00 = ms + qo, m01 = ms + (qo ^ 32), m10 = ms + (qo ^ 16), m11 = ms + (qo ^ 48);
       i32x2_t ka[kQSteps], kb[kQSteps];
       auto rd = [&](auto kc) {
         constexpr int kk = decltype(kc)::value;
         if constexpr (kk < 16) {
-          ka[kk] = lds_read_b64<2048 * (kk >> 1) + 512 * (kk & 1)>(m0);
-          kb[kk] = lds_read_b64<2048 * (kk >> 1) + 512 * (kk & 1)>(m1);
+          ka[kk] = lds_read_b64<2048 * (kk >> 1)>(kk & 1 ? m01 : m00);
+          kb[kk] = lds_read_b64<2048 * (kk >> 1) + 1024>(kk & 1 ? m11 : m10);
         } else {
-          ka[kk] = lds_read_b64<512 * (kk & 1)>(r0);
-          kb[kk] = lds_read_b64<512 * (kk & 1)>(r1);
+          ka[kk] = lds_read_b64<0>(rs + (kk & 1 ? (qo ^ 32) : qo));
+          kb[kk] = lds_read_b64<1024>(rs + (kk & 1 ? (qo ^ 48) : (qo ^ 16)));
         }
       };
       static_for<A>([&](auto kc) { rd(kc); });
@@ -444,8 +461,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kb[kk].x, kb[kk].y), qf[kk], s1, 0, 0, 0);
       });
     } else {
-      const uint32_t ma = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 16 * lane);
-      const uint32_t ra = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + 16 * lane);
+      const int qo = qk_off();
+      const uint32_t ma = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + qo);
+      const uint32_t ra = (uint32_t)(uintptr_t)(lds_void_ptr)(rope_stage(tt) + qo);
       u32x4_t ka[kQSteps], kb[kQSteps];
       auto rd = [&](auto kc) {
         constexpr int kk = decltype(kc)::value;
@@ -484,12 +502,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     if constexpr (!FP8) pb = (uint32_t)(uintptr_t)(lds_void_ptr)(s_p[tt & 1] + 16 * lane_now());
     if constexpr (FP8) {
       // features 16*(4*wave + f) + lane%16, 8 tokens in the P^T order
-      const uint32_t vb =
-          (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv8_base + 2048 * wave);
+      const uint32_t vb = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 2048 * wave);
+      const int po = po8_h;
       i32x2_t r[kFBW];
       static_for<kFBW>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        r[f] = lds_read_tr8<256 * f>(vb);
+        r[f] = lds_read_tr8<0>(vb + (po ^ (16 * f)));
       });
       lgkm_wait_4v<0>(r[0], r[1], r[2], r[3]);
 #pragma unroll
@@ -497,13 +515,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     } else {
       // ds_read_b64_tr_b16 of features 16*(4*wave + f) + lane%16 for tokens
       // 4*g4 + e (first read) and 16 + 4*g4 + e (second)
-      const uint32_t vb =
-          (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + pv_base + 4096 * wave);
+      const int po = pv_off();
+      const uint32_t vb0 = (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 4096 * wave + po);
+      const uint32_t vb1 =
+          (uint32_t)(uintptr_t)(lds_void_ptr)(main_stage(tt) + 4096 * wave + (po ^ 32));
       i32x2_t r[2 * kFBW];
       static_for<kFBW>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        r[2 * f] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1)>(vb);
-        r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 512 * (f & 1) + 1024>(vb);
+        r[2 * f] = lds_read_tr16<2048 * (f >> 1)>(f & 1 ? vb1 : vb0);
+        r[2 * f + 1] = lds_read_tr16<2048 * (f >> 1) + 1024>(f & 1 ? vb1 : vb0);
       });
       pr[0] = lds_read_b128<0>(pb);
       pr[1] = lds_read_b128<1024>(pb);
@@ -598,9 +618,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
 
   // the first kAhead tiles' slot entries are all read before a gather is issued
   auto start = [&]() {
-    int sv[Lay::kAhead][kDmaMax];
+    int sv[Lay::kAhead];
 #pragma unroll
-    for (int u = 0; u < Lay::kAhead; ++u) tile_slots(u, sv[u]);
+    for (int u = 0; u < Lay::kAhead; ++u) sv[u] = tile_slot(u);
 #pragma unroll
     for (int u = 0; u < Lay::kAhead; ++u)
       if (u < ntiles) issue(u, sv[u]);
@@ -634,9 +654,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_decode_kernel(
     const int rflag = s_restart[(t + 1) & 1];   // raised while finishing tile t-1
     const int sv = t < ntiles ? s_sring[(t % kSlotRing) * kTile + (lane & 31)] : 0;
     if (t + Lay::kAhead < ntiles) {
-      int nsv[kDmaMax];
-      tile_slots(t + Lay::kAhead, nsv);
-      issue(t + Lay::kAhead, nsv);
+      issue(t + Lay::kAhead, tile_slot(t + Lay::kAhead));
     }
     // the two matrix phases run at raised wave priority: where the two waves
     // of a SIMD are in different phases, the softmax and gather issue of one
